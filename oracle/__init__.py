@@ -1,0 +1,33 @@
+"""CPU oracle for the fused 3D RoPE (test infrastructure only).
+
+Only tests/, the graft entry point's smoke() and bench.py's cpu_baseline leg
+may import this package.  The product library (rope_ltx3drope_amd) never
+does: it fails loudly when its HIP library is missing instead of falling
+back to the CPU.
+
+Parity pins (all CPU tests, tests/test_oracle_pins.py): closed forms of the
+inverse frequencies, tables against an arbitrary-precision evaluation,
+unit-vector readback, identity at position 0, norm preservation, a +theta /
+-theta round trip, an error bound against the exact complex product, a
+brute-force per-element angle recomputation on tiny grids, the bf16 cast
+against torch's CPU cast and its closed-form properties.  Parity with
+sglang's own table bits is unpinned (no values are printed on the pages).
+"""
+from .rope import (  # noqa: F401
+    BF16,
+    F32,
+    apply_rope_tokens,
+    axis_tables,
+    bf16_bits_to_f32,
+    f32_to_bf16_bits,
+    from_f32,
+    grid_tables,
+    inv_freqs,
+    rope3d,
+    rope3d_qk,
+    rope3d_sampled,
+    rotate_pairs,
+    to_f32,
+    token_coords,
+    validate,
+)

@@ -1,0 +1,158 @@
+"""Seeded synthetic inputs for the fused 3D RoPE workloads.
+
+This module holds the workload shapes and the random-number recipes only.
+It contains none of the rotary arithmetic (no tables, no rotation, no
+rounding of results), so both the CPU oracle and the GPU path can take
+their inputs from it without sharing any of the method's code.
+
+The decoder pages measure the RoPE on LTX-2.5 decoder tiles (stage 0/4/5)
+whose exact geometries are not printed; the workloads below stand in for
+them: Q/K shaped [B, T, H, W, heads, head_dim], contiguous, with token
+n = (t*H + h)*W + w and the head dimension split into (dim_t, dim_h, dim_w)
+channels (sglang PR #35698 page, "Key source snippets", JIT wrapper: the
+six q dimensions and the per-axis table shapes of the precheck).
+
+Representation: fp32 arrays are numpy float32; bf16 arrays are numpy
+uint16 holding the raw bf16 bit patterns.  The fp32 -> bf16 conversion of
+the drawn normals is done by torch's CPU cast (round to nearest even),
+a library routine that neither the oracle nor the HIP path uses.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Iterator, List, Sequence, Tuple
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One workload: a dtype, a batch/heads/head_dim shape and one or more grids."""
+
+    key: int
+    name: str
+    dtype: str
+    B: int
+    grids: Tuple[Tuple[int, int, int], ...]
+    heads: int
+    head_dim: int
+    split: Tuple[int, int, int]
+    base: float
+    seed: int
+    dist: str  # "normal" or "normal3_outliers"
+    calls: Tuple[int, ...]  # the order in which grids are visited (indices into grids)
+
+    def shape(self, grid_index: int = 0) -> Tuple[int, int, int, int, int, int]:
+        T, H, W = self.grids[grid_index]
+        return (self.B, T, H, W, self.heads, self.head_dim)
+
+    def numel(self, grid_index: int = 0) -> int:
+        return int(np.prod(self.shape(grid_index), dtype=np.int64))
+
+    @property
+    def itemsize(self) -> int:
+        return 4 if self.dtype == F32 else 2
+
+    def algorithmic_bytes(self, grid_index: int = 0) -> int:
+        """Q and K each read once and written once."""
+        return 2 * 2 * self.numel(grid_index) * self.itemsize
+
+
+WORKLOADS = {
+    1: Workload(1, "tiny_f32_2x4x4_h2_d48", F32, 1, ((2, 4, 4),), 2, 48, (16, 16, 16),
+                10000.0, 0, "normal", (0,)),
+    2: Workload(2, "bf16_4x32x32_h16_d128", BF16, 1, ((4, 32, 32),), 16, 128, (32, 48, 48),
+                10000.0, 1, "normal", (0,)),
+    3: Workload(3, "stage4_tile_bf16_8x64x64_h24_d128_x24calls", BF16, 1, ((8, 64, 64),), 24, 128,
+                (32, 48, 48), 10000.0, 2, "normal", (0,) * 24),
+    4: Workload(4, "stage5_tile_bf16_16x96x96_h24_d128_outliers", BF16, 1, ((16, 96, 96),), 24, 128,
+                (32, 48, 48), 10000.0, 3, "normal3_outliers", (0,)),
+    5: Workload(5, "ragged_bf16_b2_17x68x120_h32_d96_3grids", BF16, 2,
+                ((17, 68, 120), (9, 68, 120), (17, 34, 60)), 32, 96, (32, 32, 32),
+                10000.0, 4, "normal", (0, 1, 2) * 4),
+}
+
+_CHUNK = 1 << 24  # elements drawn per numpy call; the stream is sequential so chunking is invisible
+
+
+def _f32_to_bf16_bits_torch(x: np.ndarray) -> np.ndarray:
+    import torch  # CPU only; used as a library cast for input generation
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _draw_normal(rng: np.random.Generator, n: int, dtype: str, scale: float | None) -> np.ndarray:
+    out = np.empty(n, dtype=np.float32 if dtype == F32 else np.uint16)
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        v = rng.standard_normal(e - s, dtype=np.float32)
+        if scale is not None:
+            v = np.multiply(v, np.float32(scale), dtype=np.float32)
+        out[s:e] = v if dtype == F32 else _f32_to_bf16_bits_torch(v)
+    return out
+
+
+def _outlier_value_bits(value: float, dtype: str):
+    if dtype == F32:
+        return np.float32(value)
+    return _f32_to_bf16_bits_torch(np.array([value], dtype=np.float32))[0]
+
+
+def generate(w: Workload, grid_indices: Sequence[int] | None = None) -> List[Tuple[np.ndarray, np.ndarray]]:
+    """Return [(q, k), ...] for the requested grids, drawn from one generator.
+
+    One numpy PCG64 generator seeded with the workload's seed draws, in
+    order and in C order: for each grid of the workload, all of Q then all
+    of K.  Grids not requested are still drawn (to keep the stream order)
+    but dropped.  For "normal3_outliers" the values are 3*N(0,1) (an fp32
+    multiply before the cast), then for Q and then K about 0.1 % of the
+    flat positions (rng.integers, duplicates allowed) are set to +60 or -60
+    with the sign drawn by rng.integers(0, 2).
+    """
+    want = set(range(len(w.grids))) if grid_indices is None else set(grid_indices)
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    out = []
+    for gi in range(len(w.grids)):
+        n = w.numel(gi)
+        scale = 3.0 if w.dist == "normal3_outliers" else None
+        q = _draw_normal(rng, n, w.dtype, scale)
+        k = _draw_normal(rng, n, w.dtype, scale)
+        if w.dist == "normal3_outliers":
+            pos = _outlier_value_bits(60.0, w.dtype)
+            neg = _outlier_value_bits(-60.0, w.dtype)
+            for x in (q, k):
+                cnt = int(round(1e-3 * n))
+                idx = rng.integers(0, n, size=cnt)
+                sign = rng.integers(0, 2, size=cnt)
+                x[idx] = np.where(sign == 1, pos, neg).astype(x.dtype)
+        if gi in want:
+            shp = w.shape(gi)
+            out.append((q.reshape(shp), k.reshape(shp)))
+    return out
+
+
+def generate_custom(shape: Sequence[int], dtype: str, seed: int, scale: float | None = None):
+    """Q, K of an arbitrary [B,T,H,W,heads,D] shape with N(0,1)*scale values (tests)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = int(np.prod(shape, dtype=np.int64))
+    q = _draw_normal(rng, n, dtype, scale).reshape(shape)
+    k = _draw_normal(rng, n, dtype, scale).reshape(shape)
+    return q, k
+
+
+def sample_tokens(num_tokens: int, count: int, seed: int) -> np.ndarray:
+    """Sorted distinct flat token indices (b*N + n) used for sampled comparisons."""
+    rng = np.random.Generator(np.random.PCG64(seed + 1_000_003))
+    count = min(count, num_tokens)
+    idx = rng.choice(num_tokens, size=count, replace=False)
+    # always include the first and last token so both ends of the tensor are checked
+    idx = np.unique(np.concatenate([idx, [0, num_tokens - 1]]))
+    return idx.astype(np.int64)
+
+
+def iter_calls(w: Workload) -> Iterator[int]:
+    yield from w.calls
