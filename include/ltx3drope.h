@@ -1,0 +1,225 @@
+/*
+ * ltx3drope.h - fused 3D rotary position embedding (RoPE) of the LTX-2.5
+ * diffusion video decoder, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one described on the sglang PR #35698 page
+ * ("fused LTX-2.5 decoder 3D RoPE", prhub.com.cn): sections "Implementation
+ * breakdown" (steps 1-4) and "Key source snippets" (the JIT wrapper and the
+ * CUDA kernel).  Every decoder attention block rotates its Q and K over the
+ * latent (T, H, W) token grid with per-axis cos/sin tables that all blocks
+ * on one grid share.
+ *
+ * Tensor layout (all four tensors): contiguous [B, T, H, W, heads, head_dim]
+ * of one dtype; token n = (t*H + h)*W + w inside each batch element.  The
+ * head dimension is cut into a t chunk of dim_t channels, an h chunk of
+ * dim_h channels and a w chunk of dim_w channels, in that order
+ * (head_dim == dim_t + dim_h + dim_w, each even and > 0).  Inside a chunk the
+ * channels form interleaved pairs (x[2j], x[2j+1]).
+ *
+ * Tables: for an axis of length L and width d, entry (p, i), p in [0, L),
+ * i in [0, d/2), holds cos and sin of p * base^(-2i/d), evaluated in float64
+ * on the host and rounded once to fp32.  (The page names the builder but not
+ * its formula; this is the textbook inverse-frequency reading with integer,
+ * tile-local positions, since the cache key has no offset.)
+ *
+ * Rotation of one pair (e, o) with (c, s) from the token's table row, every
+ * operation an fp32 IEEE round-to-nearest-even step and no fused
+ * multiply-add ("Key source snippets", the kernel's pair-rotation helper):
+ *     e' = (e*c) - (o*s),   o' = (e*s) + (o*c)
+ * then cast back to the tensor dtype (bf16: round to nearest, ties to even;
+ * fp32: identity).  Q and K use the same (c, s).  Results are written out of
+ * place; inputs are never modified.
+ *
+ * All functions are thread-safe, never throw, and return a status code
+ * (LTX3DROPE_OK == 0, negative on error) unless stated otherwise.  Pointers
+ * named q, k, q_out, k_out are device pointers owned by the caller.  Table
+ * handles are owned by the library and reference counted.  A "stream" is a
+ * hipStream_t passed as void* (NULL = the device's null stream).
+ */
+#ifndef LTX3DROPE_H
+#define LTX3DROPE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LTX3DROPE_VERSION 1
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+    LTX3DROPE_OK = 0,
+    LTX3DROPE_E_INVALID = -1,        /* an argument is malformed (null handle, bad size, bad base) */
+    LTX3DROPE_E_UNSUPPORTED = -2,    /* the precheck rejects the tensors; nothing was launched */
+    LTX3DROPE_E_TABLE_MISMATCH = -3, /* the tables do not belong to this grid / split / device */
+    LTX3DROPE_E_HIP = -4,            /* a HIP runtime call failed */
+    LTX3DROPE_E_NOMEM = -5           /* a host or device allocation failed */
+};
+
+/* ---- element types ----------------------------------------------------- */
+enum { LTX3DROPE_DTYPE_F32 = 0, LTX3DROPE_DTYPE_BF16 = 1 };
+
+/* ---- precheck reason codes (ltx3drope_can_use) ------------------------- */
+enum {
+    LTX3DROPE_REASON_OK = 0,
+    LTX3DROPE_REASON_NULLPTR = 1,        /* a tensor pointer or the table handle is NULL */
+    LTX3DROPE_REASON_DTYPE = 2,          /* dtype is neither F32 nor BF16 */
+    LTX3DROPE_REASON_NONPOSITIVE_DIM = 3,/* B, T, H, W, heads or head_dim <= 0 */
+    LTX3DROPE_REASON_SPLIT_ODD = 4,      /* a table chunk width is odd or <= 0 (tables carry the split) */
+    LTX3DROPE_REASON_SPLIT_SUM = 5,      /* head_dim != dim_t + dim_h + dim_w */
+    LTX3DROPE_REASON_TABLE_GRID = 6,     /* the tables were built for another (T, H, W) */
+    LTX3DROPE_REASON_TABLE_DEVICE = 7,   /* the tables live on another device than the tensors */
+    LTX3DROPE_REASON_ALIGN = 8,          /* a pointer is not aligned to one pair (2 elements) */
+    LTX3DROPE_REASON_OVERLAP = 9,        /* an output overlaps an input or the other output */
+    LTX3DROPE_REASON_TOO_LARGE = 10,     /* B*T*H*W*heads*head_dim >= 2^31 elements */
+    LTX3DROPE_REASON_NOT_DEVICE_PTR = 11,/* a pointer is not device memory of the tables' device */
+    LTX3DROPE_REASON_HOST_MODE = 12,     /* the library is in host-table test mode (no launches) */
+    LTX3DROPE_REASON_EXTENT = 13         /* a pointer's device allocation ends before the tensor does */
+};
+
+/* ---- options (ltx3drope_set_option / ltx3drope_get_option) ------------- */
+enum {
+    LTX3DROPE_OPT_PATH = 1,        /* 0 auto (gate decides), 1 force fast kernel, 2 force plain kernel */
+    LTX3DROPE_OPT_GATE = 2,        /* 0 off (trust fast), 1 verify the first call per key (default), 2 verify every call */
+    LTX3DROPE_OPT_FORCE_GATE_MISMATCH = 3, /* 1: every verification reports a mismatch (tests the fallback) */
+    LTX3DROPE_OPT_HOST_TABLES = 4, /* 1: tables are built in host memory and nothing touches HIP (CPU tests of the
+                                      cache and the precheck); apply_qk then refuses with REASON_HOST_MODE */
+    LTX3DROPE_OPT_LOG = 5          /* 1: one stderr line per gate decision */
+};
+
+/* ---- gate states (ltx3drope_gate_state) -------------------------------- */
+enum { LTX3DROPE_GATE_UNSEEN = 0, LTX3DROPE_GATE_TRUSTED = 1, LTX3DROPE_GATE_DISABLED = 2 };
+
+typedef struct ltx3drope_tables* ltx3drope_tables_t;
+
+typedef struct {
+    int device;
+    int64_t T, H, W;
+    int64_t dim_t, dim_h, dim_w;
+    double base;
+    /* device (or, in host-table mode, host) address of the packed tables: float pairs (cos, sin),
+       t section [T][dim_t/2], then h section [H][dim_h/2], then w section [W][dim_w/2] */
+    const void* packed;
+    int64_t packed_pairs;
+} ltx3drope_tables_desc;
+
+typedef struct {
+    int64_t cache_hits, cache_misses, cache_evictions, cache_live;
+    int64_t tables_alive;               /* table objects not yet freed (cache- or caller-held) */
+    int64_t gate_verifications, gate_trusted, gate_disabled;
+    int64_t fast_launches, plain_launches;
+    int64_t rejected;                   /* apply_qk calls refused by the precheck */
+} ltx3drope_stats_t;
+
+/*
+ * ltx3drope_tables_build - find or build the per-axis tables of one grid.
+ *
+ * The page's cached table lookup ("Implementation breakdown", step 1): the key
+ * is (device, T, H, W, dim_t, dim_h, dim_w, base); a hit returns the cached
+ * tables; a miss builds them (float64 on the host, rounded once to fp32),
+ * uploads them with hipMemcpyAsync on `stream` followed by a synchronization of
+ * that stream, and inserts them.  The cache holds at most 16 entries and
+ * evicts first-in first-out (a hit does not refresh an entry).
+ *
+ * On success *out receives a handle holding one reference for the caller;
+ * release it with ltx3drope_tables_release.  Eviction only drops the cache's
+ * own reference, so a handle held by a caller stays valid after eviction.
+ * Errors: E_INVALID (null out, T/H/W <= 0, a dim odd or <= 0, base not finite
+ * or <= 0, device < 0), E_NOMEM, E_HIP.
+ */
+int ltx3drope_tables_build(int device, int64_t T, int64_t H, int64_t W,
+                           int64_t dim_t, int64_t dim_h, int64_t dim_w, double base,
+                           void* stream, ltx3drope_tables_t* out);
+
+/* Drop one reference; the table memory is freed when the last one goes (hipFree waits for the
+   device's outstanding work).  E_INVALID on NULL. */
+int ltx3drope_tables_release(ltx3drope_tables_t tables);
+
+/* Describe a table set (grid, split, base, device, packed address).  E_INVALID on NULL arguments. */
+int ltx3drope_tables_describe(ltx3drope_tables_t tables, ltx3drope_tables_desc* out);
+
+/* Copy the six tables to caller-owned host arrays of fp32, row-major [L][d/2] each (any pointer may
+   be NULL to skip it).  Synchronous (device-wide copy).  E_INVALID, E_HIP. */
+int ltx3drope_tables_read(ltx3drope_tables_t tables, float* cos_t, float* sin_t, float* cos_h,
+                          float* sin_h, float* cos_w, float* sin_w);
+
+/* Drop the cache's references to every entry (tables still held by callers stay valid). */
+int ltx3drope_cache_clear(void);
+
+/*
+ * ltx3drope_can_use - the precheck ("Key source snippets", the JIT wrapper's
+ * can_use predicate, plus rules of this library).
+ *
+ * Returns 1 if ltx3drope_apply_qk would launch for these arguments, 0 if it
+ * would refuse.  q_out and k_out may both be NULL: then only the inputs are
+ * checked (for a caller that allocates fresh outputs afterwards); when `reason` is not NULL it receives an LTX3DROPE_REASON_*
+ * code (the first failing rule in the order of the enum).  Rules: no NULL
+ * pointer or handle; dtype F32 or BF16; B, T, H, W, heads, head_dim > 0;
+ * table split widths even and > 0 and summing to head_dim; tables built for
+ * (T, H, W); every pointer aligned to one pair (8 B for F32, 4 B for BF16);
+ * neither output overlapping an input or the other output; fewer than 2^31
+ * elements per tensor; all four pointers device memory of the tables'
+ * device, each inside an allocation large enough for the whole tensor
+ * (checked last, REASON_NOT_DEVICE_PTR then REASON_EXTENT; skipped in
+ * host-table mode).  Pure host logic: no launch, no allocation, no synchronization
+ * (pointer attributes are queried from the HIP runtime).
+ */
+int ltx3drope_can_use(const void* q_out, const void* k_out, const void* q, const void* k, int dtype,
+                      int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
+                      ltx3drope_tables_t tables, int* reason);
+
+/*
+ * ltx3drope_apply_qk - rotate Q and K in one launch ("Key source snippets":
+ * the wrapper writes fresh q_out and k_out with one kernel launch).
+ *
+ * q, k: inputs [B, T, H, W, heads, head_dim]; q_out, k_out: caller-allocated
+ * outputs of the same shape and dtype (the caller allocates them fresh; they
+ * must not overlap the inputs).  The precheck runs first; on failure nothing
+ * is launched and E_UNSUPPORTED (or E_TABLE_MISMATCH for REASON_TABLE_GRID /
+ * REASON_TABLE_DEVICE) is returned.  Otherwise the work is enqueued on
+ * `stream` and the call returns without waiting, except on the first call of
+ * a configuration while the bit-exact gate is on: then the fast kernel's
+ * output is checked bit for bit against the plain kernel on the device and
+ * the stream is synchronized once ("Implementation breakdown", step 4: first
+ * call verified; equal -> the fast path is trusted, unequal -> permanent
+ * fallback to the plain path for that configuration).  The gate's
+ * configuration key is (device, dtype, B, T, H, W, heads, head_dim, dim_t,
+ * dim_h, dim_w).
+ */
+int ltx3drope_apply_qk(void* q_out, void* k_out, const void* q, const void* k, int dtype,
+                       int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
+                       ltx3drope_tables_t tables, void* stream);
+
+/* Gate state of one configuration key (LTX3DROPE_GATE_*), or a negative status. */
+int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W,
+                         int64_t heads, int64_t head_dim, int64_t dim_t, int64_t dim_h, int64_t dim_w);
+
+/* Forget every gate decision (all configurations become UNSEEN). */
+int ltx3drope_gate_reset(void);
+
+int ltx3drope_set_option(int option, int64_t value);
+int64_t ltx3drope_get_option(int option);
+
+int ltx3drope_stats(ltx3drope_stats_t* out);
+int ltx3drope_stats_reset(void);
+
+/* Which kernel apply_qk would use for these arguments when the gate trusts the fast path:
+   1 fast, 2 plain, or a negative status if the precheck fails. */
+int ltx3drope_kernel_choice(const void* q_out, const void* k_out, const void* q, const void* k,
+                            int dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads,
+                            int64_t head_dim, ltx3drope_tables_t tables);
+
+/* Measurement helper: copy `bytes` (a multiple of 16, both pointers 16-B aligned) from src to dst
+   with a plain streaming kernel on `stream`; used to calibrate bandwidth and traffic counters. */
+int ltx3drope_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+const char* ltx3drope_status_string(int status);
+const char* ltx3drope_reason_string(int reason);
+int ltx3drope_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LTX3DROPE_H */

@@ -1,0 +1,274 @@
+"""rope_ltx3drope_amd: fused 3D RoPE of the LTX-2.5 diffusion video decoder on MI355X.
+
+Thin Python binding of the ltx3drope C ABI (include/ltx3drope.h).  Every step
+of the operation -- table construction and caching, the precheck, the gate and
+the rotation kernels -- runs in the native library; this module only marshals
+arguments.  PyTorch supplies device memory (torch.empty_like for the fresh
+outputs, as the page's wrapper does) and the current HIP stream.  If the
+library is missing, every call raises: there is no CPU fallback.
+
+Names follow the sglang PR #35698 page ("Implementation breakdown", steps 1-4;
+"Key source snippets"): tables() is the cached per-axis table lookup,
+can_use() the precheck, apply_qk() the fused one-launch rotation of Q and K and
+forward_pair() the decoder-side entry that ties them together.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_F32,
+    GATE_STATES,
+    OPT_FORCE_GATE_MISMATCH,
+    OPT_GATE,
+    OPT_HOST_TABLES,
+    OPT_LOG,
+    OPT_PATH,
+    REASON_CODES,
+    REASONS,
+)
+
+__all__ = [
+    "Ltx3dRopeError", "Ltx3dRopeUnsupported", "Tables", "tables", "tables_build", "can_use", "apply_qk",
+    "forward_pair", "kernel_choice", "stats", "stats_reset", "set_option", "get_option", "gate_state", "gate_reset",
+    "cache_clear", "copy_bytes", "version",
+]
+
+
+class Ltx3dRopeError(RuntimeError):
+    """A library call failed (status code in .status)."""
+
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_lib.status_string(status)} ({status})")
+        self.status = status
+
+
+class Ltx3dRopeUnsupported(Ltx3dRopeError):
+    """The precheck rejected the inputs; nothing was launched (reason name in .reason)."""
+
+    def __init__(self, reason: str, status: int = _lib.E_UNSUPPORTED):
+        RuntimeError.__init__(self, f"unsupported input: {reason}")
+        self.status = status
+        self.reason = reason
+
+
+def _check(status: int, what: str) -> None:
+    if status != _lib.OK:
+        raise Ltx3dRopeError(status, what)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    return -1
+
+
+def _stream_ptr(device, stream=None) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+class Tables:
+    """A reference to one cached table set (released on close() / garbage collection)."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if not self._h:
+            raise ValueError("tables already released")
+        return self._h
+
+    def describe(self) -> dict:
+        d = _lib.TablesDesc()
+        _check(_lib.lib().ltx3drope_tables_describe(self.handle, ctypes.byref(d)), "tables_describe")
+        return {"device": d.device, "grid": (d.T, d.H, d.W), "split": (d.dim_t, d.dim_h, d.dim_w), "base": d.base,
+                "packed": d.packed, "packed_pairs": d.packed_pairs}
+
+    @property
+    def grid(self) -> Tuple[int, int, int]:
+        return self.describe()["grid"]
+
+    @property
+    def split(self) -> Tuple[int, int, int]:
+        return self.describe()["split"]
+
+    def read(self):
+        """The six tables as numpy fp32 arrays ((cos_t, sin_t), (cos_h, sin_h), (cos_w, sin_w))."""
+        import numpy as np
+
+        d = self.describe()
+        shapes = [(L, dd // 2) for L, dd in zip(d["grid"], d["split"])]
+        arrs = [np.empty(s, np.float32) for s in shapes for _ in range(2)]
+        ptrs = [a.ctypes.data_as(_lib.fp) for a in arrs]
+        _check(_lib.lib().ltx3drope_tables_read(self.handle, *ptrs), "tables_read")
+        return (arrs[0], arrs[1]), (arrs[2], arrs[3]), (arrs[4], arrs[5])
+
+    def close(self) -> None:
+        if self._h:
+            _lib.lib().ltx3drope_tables_release(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def tables_build(T: int, H: int, W: int, split: Sequence[int], base: float = 10000.0, device: int = 0,
+                 stream=None) -> Tables:
+    """Find or build the per-axis tables of a (T, H, W) grid (FIFO cache of 16 entries)."""
+    dt, dh, dw = (int(x) for x in split)
+    out = ctypes.c_void_p()
+    host_mode = get_option(OPT_HOST_TABLES) != 0
+    sp = 0 if host_mode else _stream_ptr(_torch().device("cuda", device), stream)
+    _check(_lib.lib().ltx3drope_tables_build(int(device), int(T), int(H), int(W), dt, dh, dw, float(base), sp,
+                                              ctypes.byref(out)), "tables_build")
+    return Tables(out.value)
+
+
+tables = tables_build
+
+
+def _shape6(q):
+    if q.dim() != 6:
+        raise Ltx3dRopeUnsupported("NOT_6D")
+    return tuple(int(s) for s in q.shape)
+
+
+def _marshal(q, k, q_out, k_out):
+    if k.shape != q.shape:
+        raise Ltx3dRopeUnsupported("SHAPE_MISMATCH")
+    if k.dtype != q.dtype:
+        raise Ltx3dRopeUnsupported("DTYPE")
+    if not (q.is_cuda and k.is_cuda) or q.device != k.device:
+        raise Ltx3dRopeUnsupported("NOT_DEVICE_PTR")
+    for t in (q, k, q_out, k_out):
+        if t is not None and not t.is_contiguous():
+            raise Ltx3dRopeUnsupported("NOT_CONTIGUOUS")
+    for t in (q_out, k_out):
+        if t is not None and (t.shape != q.shape or t.dtype != q.dtype or t.device != q.device):
+            raise Ltx3dRopeUnsupported("OUTPUT_MISMATCH")
+
+
+def can_use(q, k, tabs: Tables, q_out=None, k_out=None) -> Tuple[bool, str]:
+    """The precheck: (True, "OK") if apply_qk would launch, else (False, reason)."""
+    try:
+        B, T, H, W, heads, D = _shape6(q)
+        _marshal(q, k, q_out, k_out)
+    except Ltx3dRopeUnsupported as e:
+        return False, e.reason
+    qo = q_out.data_ptr() if q_out is not None else None
+    ko = k_out.data_ptr() if k_out is not None else None
+    if (qo is None) != (ko is None):
+        raise ValueError("give both q_out and k_out, or neither")
+    reason = ctypes.c_int(0)
+    ok = _lib.lib().ltx3drope_can_use(qo, ko, q.data_ptr(), k.data_ptr(), _dtype_code(q), B, T, H, W, heads, D,
+                                      tabs.handle, ctypes.byref(reason))
+    return bool(ok), _lib.REASONS.get(reason.value, str(reason.value))
+
+
+def apply_qk(q, k, tabs: Tables, q_out=None, k_out=None, stream=None):
+    """Rotate Q and K into fresh (or the given) output tensors with one kernel launch."""
+    torch = _torch()
+    B, T, H, W, heads, D = _shape6(q)
+    _marshal(q, k, q_out, k_out)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if k_out is None:
+        k_out = torch.empty_like(k)
+    st = _lib.lib().ltx3drope_apply_qk(q_out.data_ptr(), k_out.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                       _dtype_code(q), B, T, H, W, heads, D, tabs.handle,
+                                       _stream_ptr(q.device, stream))
+    if st in (_lib.E_UNSUPPORTED, _lib.E_TABLE_MISMATCH):
+        reason = ctypes.c_int(0)
+        _lib.lib().ltx3drope_can_use(q_out.data_ptr(), k_out.data_ptr(), q.data_ptr(), k.data_ptr(),
+                                     _dtype_code(q), B, T, H, W, heads, D, tabs.handle, ctypes.byref(reason))
+        raise Ltx3dRopeUnsupported(_lib.REASONS.get(reason.value, str(reason.value)), st)
+    _check(st, "apply_qk")
+    return q_out, k_out
+
+
+def forward_pair(q, k, split: Sequence[int], base: float = 10000.0, q_out=None, k_out=None, stream=None):
+    """Decoder-side entry: cached tables for q's (T, H, W) grid, then the fused rotation."""
+    B, T, H, W, heads, D = _shape6(q)
+    with tables_build(T, H, W, split, base, device=q.device.index or 0, stream=stream) as tabs:
+        return apply_qk(q, k, tabs, q_out, k_out, stream)
+
+
+def kernel_choice(q, k, tabs: Tables, q_out=None, k_out=None) -> str:
+    """'fast' or 'plain': the kernel apply_qk uses once the gate trusts the fast path."""
+    torch = _torch()
+    B, T, H, W, heads, D = _shape6(q)
+    qo = q_out if q_out is not None else torch.empty_like(q)
+    ko = k_out if k_out is not None else torch.empty_like(k)
+    r = _lib.lib().ltx3drope_kernel_choice(qo.data_ptr(), ko.data_ptr(), q.data_ptr(), k.data_ptr(), _dtype_code(q),
+                                           B, T, H, W, heads, D, tabs.handle)
+    if r < 0:
+        raise Ltx3dRopeError(r, "kernel_choice")
+    return {1: "fast", 2: "plain"}[r]
+
+
+def stats() -> dict:
+    s = _lib.Stats()
+    _check(_lib.lib().ltx3drope_stats(ctypes.byref(s)), "stats")
+    return s.as_dict()
+
+
+def stats_reset() -> None:
+    _check(_lib.lib().ltx3drope_stats_reset(), "stats_reset")
+
+
+def set_option(option: int, value: int) -> None:
+    _check(_lib.lib().ltx3drope_set_option(int(option), int(value)), "set_option")
+
+
+def get_option(option: int) -> int:
+    return int(_lib.lib().ltx3drope_get_option(int(option)))
+
+
+def gate_state(device: int, dtype: int, shape: Sequence[int], split: Sequence[int]) -> str:
+    r = _lib.lib().ltx3drope_gate_state(int(device), int(dtype), *[int(s) for s in shape], *[int(s) for s in split])
+    if r < 0:
+        raise Ltx3dRopeError(r, "gate_state")
+    return GATE_STATES[r]
+
+
+def gate_reset() -> None:
+    _check(_lib.lib().ltx3drope_gate_reset(), "gate_reset")
+
+
+def cache_clear() -> None:
+    _check(_lib.lib().ltx3drope_cache_clear(), "cache_clear")
+
+
+def copy_bytes(dst, src, nbytes: Optional[int] = None, stream=None) -> None:
+    """Plain streaming copy kernel (bandwidth and counter calibration)."""
+    n = int(nbytes if nbytes is not None else src.numel() * src.element_size())
+    _check(_lib.lib().ltx3drope_copy(dst.data_ptr(), src.data_ptr(), n, _stream_ptr(src.device, stream)), "copy")
+
+
+def version() -> int:
+    return int(_lib.lib().ltx3drope_version())

@@ -1,0 +1,517 @@
+// C ABI of the ltx3drope library: precheck, bit-exact gate, dispatch, options,
+// statistics.
+//
+// Precheck: sglang PR #35698 page, "Key source snippets", the JIT wrapper's
+// can_use predicate (6-D shapes, dtype, same device, positive sizes, head_dim
+// equal to the split sum, even positive chunk widths, contiguity, pointer
+// alignment, per-axis table shapes and device).  Contiguity is implied by the
+// C ABI (plain pointers to contiguous tensors); this library adds the overlap,
+// index-width and allocation-extent rules.
+//
+// Gate: same page, "Implementation breakdown", step 4: the first time a
+// configuration is seen, the fast result is compared bit for bit with the
+// reference path; equal -> trusted from then on, unequal -> that configuration
+// permanently falls back to the reference path.  Here the reference path is
+// the plain HIP kernel and the comparison runs on the device.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "internal.h"
+
+namespace ltx3drope {
+namespace {
+
+// ---- options ---------------------------------------------------------------
+
+struct Options {
+    std::atomic<int64_t> path{0};
+    std::atomic<int64_t> gate{1};
+    std::atomic<int64_t> force_mismatch{0};
+    std::atomic<int64_t> host_tables{0};
+    std::atomic<int64_t> log{0};
+    Options() {
+        if (const char* s = std::getenv("LTX3DROPE_PATH")) {
+            if (!std::strcmp(s, "fast")) path = 1;
+            if (!std::strcmp(s, "plain")) path = 2;
+        }
+        if (const char* s = std::getenv("LTX3DROPE_GATE")) {
+            if (!std::strcmp(s, "off")) gate = 0;
+            if (!std::strcmp(s, "always")) gate = 2;
+        }
+        if (const char* s = std::getenv("LTX3DROPE_LOG")) log = std::atoi(s) != 0;
+    }
+};
+
+Options& opts() {
+    static Options* o = new Options();
+    return *o;
+}
+
+// ---- statistics ------------------------------------------------------------
+
+struct Stats {
+    std::atomic<int64_t> verifications{0}, trusted{0}, disabled{0}, fast{0}, plain{0}, rejected{0};
+};
+
+Stats& stats() {
+    static Stats* s = new Stats();
+    return *s;
+}
+
+// ---- gate ------------------------------------------------------------------
+
+using GateKey = std::tuple<int, int, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t>;
+
+struct Gate {
+    std::mutex mu;
+    std::map<GateKey, int> state;
+};
+
+Gate& gate() {
+    static Gate* g = new Gate();
+    return *g;
+}
+
+int gate_get(const GateKey& key) {
+    std::lock_guard<std::mutex> lock(gate().mu);
+    auto it = gate().state.find(key);
+    return it == gate().state.end() ? LTX3DROPE_GATE_UNSEEN : it->second;
+}
+
+void gate_set(const GateKey& key, int s) {
+    std::lock_guard<std::mutex> lock(gate().mu);
+    gate().state[key] = s;
+}
+
+// ---- per-device resources ---------------------------------------------------
+
+struct DeviceRes {
+    unsigned* counter = nullptr;  // mismatch counter of the gate's verification
+};
+
+std::mutex g_dev_mu;
+std::map<int, DeviceRes> g_dev;
+
+int device_res(int device, DeviceRes** out) {
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DeviceRes& r = g_dev[device];
+    if (r.counter == nullptr) {
+        void* mem = nullptr;
+        if (hipMalloc(&mem, 256) != hipSuccess) {
+            (void)hipGetLastError();
+            return LTX3DROPE_E_NOMEM;
+        }
+        r.counter = static_cast<unsigned*>(mem);
+    }
+    *out = &r;
+    return LTX3DROPE_OK;
+}
+
+// ---- precheck --------------------------------------------------------------
+
+bool ranges_overlap(const void* a, size_t an, const void* b, size_t bn) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+// Is p device memory of `device` inside an allocation that holds [p, p + bytes)?
+// Returns NOT_DEVICE_PTR, TABLE_DEVICE (memory of another device), EXTENT or OK.
+int check_device_ptr(const void* p, size_t bytes, int device) {
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return LTX3DROPE_REASON_NOT_DEVICE_PTR;
+    }
+    if (attr.type != hipMemoryTypeDevice) return LTX3DROPE_REASON_NOT_DEVICE_PTR;
+    if (attr.device != device) return LTX3DROPE_REASON_TABLE_DEVICE;
+    void* base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+        (void)hipGetLastError();
+        return LTX3DROPE_REASON_NOT_DEVICE_PTR;
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+    if (q < b || q + bytes > b + size) return LTX3DROPE_REASON_EXTENT;
+    return LTX3DROPE_REASON_OK;
+}
+
+// The precheck.  With check_outputs false, q_out and k_out are ignored (the caller
+// will allocate fresh outputs, which cannot overlap anything).
+int precheck(const void* q_out, const void* k_out, const void* q, const void* k, int dtype, int64_t B, int64_t T,
+             int64_t H, int64_t W, int64_t heads, int64_t D, const ltx3drope_tables* tab, bool check_memory,
+             bool check_outputs = true) {
+    if ((check_outputs && (!q_out || !k_out)) || !q || !k || !tab) return LTX3DROPE_REASON_NULLPTR;
+    if (dtype != LTX3DROPE_DTYPE_F32 && dtype != LTX3DROPE_DTYPE_BF16) return LTX3DROPE_REASON_DTYPE;
+    if (B <= 0 || T <= 0 || H <= 0 || W <= 0 || heads <= 0 || D <= 0) return LTX3DROPE_REASON_NONPOSITIVE_DIM;
+    if (tab->dim_t <= 0 || tab->dim_h <= 0 || tab->dim_w <= 0 || tab->dim_t % 2 || tab->dim_h % 2 || tab->dim_w % 2)
+        return LTX3DROPE_REASON_SPLIT_ODD;
+    if (D != tab->dim_t + tab->dim_h + tab->dim_w) return LTX3DROPE_REASON_SPLIT_SUM;
+    if (tab->T != T || tab->H != H || tab->W != W) return LTX3DROPE_REASON_TABLE_GRID;
+    const size_t es = dtype == LTX3DROPE_DTYPE_F32 ? 4 : 2;
+    const uintptr_t pair = 2 * es;
+    const void* ptrs[4] = {q, k, q_out, k_out};
+    const int nptr = check_outputs ? 4 : 2;
+    for (int i = 0; i < nptr; ++i)
+        if (reinterpret_cast<uintptr_t>(ptrs[i]) % pair) return LTX3DROPE_REASON_ALIGN;
+    // size limit before any product can overflow: each factor < 2^31 and the running product < 2^31
+    const int64_t lim = int64_t(1) << 31;
+    int64_t numel = 1;
+    for (int64_t f : {B, T, H, W, heads, D}) {
+        if (f >= lim || numel > lim / f) return LTX3DROPE_REASON_TOO_LARGE;
+        numel *= f;
+    }
+    if (numel >= lim) return LTX3DROPE_REASON_TOO_LARGE;
+    const size_t bytes = static_cast<size_t>(numel) * es;
+    if (check_outputs &&
+        (ranges_overlap(q_out, bytes, q, bytes) || ranges_overlap(q_out, bytes, k, bytes) ||
+         ranges_overlap(k_out, bytes, q, bytes) || ranges_overlap(k_out, bytes, k, bytes) ||
+         ranges_overlap(q_out, bytes, k_out, bytes)))
+        return LTX3DROPE_REASON_OVERLAP;
+    if (check_memory && !tab->host) {
+        for (int i = 0; i < nptr; ++i) {
+            const int r = check_device_ptr(ptrs[i], bytes, tab->device);
+            if (r != LTX3DROPE_REASON_OK) return r;
+        }
+    }
+    return LTX3DROPE_REASON_OK;
+}
+
+Problem make_problem(void* q_out, void* k_out, const void* q, const void* k, int dtype, int64_t B, int64_t T,
+                     int64_t H, int64_t W, int64_t heads, int64_t D, const ltx3drope_tables* tab) {
+    Problem p;
+    p.q_out = q_out;
+    p.k_out = k_out;
+    p.q = q;
+    p.k = k;
+    p.tab = tab->packed;
+    p.dtype = dtype;
+    p.B = static_cast<uint32_t>(B);
+    p.T = static_cast<uint32_t>(T);
+    p.H = static_cast<uint32_t>(H);
+    p.W = static_cast<uint32_t>(W);
+    p.heads = static_cast<uint32_t>(heads);
+    p.D = static_cast<uint32_t>(D);
+    p.PT = static_cast<uint32_t>(tab->dim_t / 2);
+    p.PH = static_cast<uint32_t>(tab->dim_h / 2);
+    p.PW = static_cast<uint32_t>(tab->dim_w / 2);
+    p.tab_pairs = static_cast<uint32_t>(tab->pairs);
+    return p;
+}
+
+int status_for_reason(int reason) {
+    if (reason == LTX3DROPE_REASON_TABLE_GRID || reason == LTX3DROPE_REASON_TABLE_DEVICE)
+        return LTX3DROPE_E_TABLE_MISMATCH;
+    return LTX3DROPE_E_UNSUPPORTED;
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+    int prev = -1;
+    explicit DeviceGuard(int device) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != device) (void)hipSetDevice(device);
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+int run_kernel(Kernel which, const Problem& p, hipStream_t stream, int device) {
+    const hipError_t e = which == Kernel::Fast ? launch_fast(p, stream, device) : launch_plain(p, stream, device);
+    if (e != hipSuccess || hipGetLastError() != hipSuccess) return LTX3DROPE_E_HIP;
+    (which == Kernel::Fast ? stats().fast : stats().plain).fetch_add(1);
+    return LTX3DROPE_OK;
+}
+
+// Fast kernel into the outputs, then the plain kernel re-derives every pair on the
+// device and counts disagreements.  Returns a status; *equal receives the verdict.
+int verify_fast(const Problem& p, hipStream_t stream, int device, bool* equal) {
+    DeviceRes* res = nullptr;
+    int st = device_res(device, &res);
+    if (st != LTX3DROPE_OK) return st;
+    st = run_kernel(Kernel::Fast, p, stream, device);
+    if (st != LTX3DROPE_OK) return st;
+    if (launch_zero_u32(res->counter, stream) != hipSuccess) return LTX3DROPE_E_HIP;
+    if (launch_verify(p, res->counter, stream, device) != hipSuccess || hipGetLastError() != hipSuccess)
+        return LTX3DROPE_E_HIP;
+    unsigned host_count = 0;
+    if (hipMemcpyAsync(&host_count, res->counter, sizeof(unsigned), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return LTX3DROPE_E_HIP;
+    }
+    stats().verifications.fetch_add(1);
+    if (opts().force_mismatch.load() != 0 && host_count == 0) host_count = 1;
+    *equal = host_count == 0;
+    if (opts().log.load() != 0)
+        std::fprintf(stderr, "[ltx3drope] gate: fast kernel %s the plain kernel (%u differing pairs)\n",
+                     *equal ? "matches" : "DIFFERS from", host_count);
+    return LTX3DROPE_OK;
+}
+
+}  // namespace
+
+int64_t option(int which) {
+    switch (which) {
+        case LTX3DROPE_OPT_PATH: return opts().path.load();
+        case LTX3DROPE_OPT_GATE: return opts().gate.load();
+        case LTX3DROPE_OPT_FORCE_GATE_MISMATCH: return opts().force_mismatch.load();
+        case LTX3DROPE_OPT_HOST_TABLES: return opts().host_tables.load();
+        case LTX3DROPE_OPT_LOG: return opts().log.load();
+        default: return LTX3DROPE_E_INVALID;
+    }
+}
+
+}  // namespace ltx3drope
+
+using namespace ltx3drope;
+
+extern "C" {
+
+int ltx3drope_tables_build(int device, int64_t T, int64_t H, int64_t W, int64_t dim_t, int64_t dim_h, int64_t dim_w,
+                           double base, void* stream, ltx3drope_tables_t* out) {
+    return tables_build(device, T, H, W, dim_t, dim_h, dim_w, base, static_cast<hipStream_t>(stream), out);
+}
+
+int ltx3drope_tables_release(ltx3drope_tables_t tables) { return tables_release(tables); }
+
+int ltx3drope_tables_describe(ltx3drope_tables_t t, ltx3drope_tables_desc* out) {
+    if (t == nullptr || out == nullptr) return LTX3DROPE_E_INVALID;
+    out->device = t->device;
+    out->T = t->T;
+    out->H = t->H;
+    out->W = t->W;
+    out->dim_t = t->dim_t;
+    out->dim_h = t->dim_h;
+    out->dim_w = t->dim_w;
+    out->base = t->base;
+    out->packed = t->packed;
+    out->packed_pairs = t->pairs;
+    return LTX3DROPE_OK;
+}
+
+int ltx3drope_tables_read(ltx3drope_tables_t t, float* cos_t, float* sin_t, float* cos_h, float* sin_h, float* cos_w,
+                          float* sin_w) {
+    if (t == nullptr) return LTX3DROPE_E_INVALID;
+    const size_t n = static_cast<size_t>(2 * t->pairs);
+    float* host = static_cast<float*>(std::malloc(n * sizeof(float)));
+    if (host == nullptr) return LTX3DROPE_E_NOMEM;
+    if (t->host) {
+        std::memcpy(host, t->packed, n * sizeof(float));
+    } else {
+        DeviceGuard guard(t->device);
+        if (hipMemcpy(host, t->packed, n * sizeof(float), hipMemcpyDeviceToHost) != hipSuccess) {
+            (void)hipGetLastError();
+            std::free(host);
+            return LTX3DROPE_E_HIP;
+        }
+    }
+    const int64_t sections[3][2] = {{t->T, t->dim_t / 2}, {t->H, t->dim_h / 2}, {t->W, t->dim_w / 2}};
+    float* outs[3][2] = {{cos_t, sin_t}, {cos_h, sin_h}, {cos_w, sin_w}};
+    size_t off = 0;
+    for (int a = 0; a < 3; ++a) {
+        const int64_t cnt = sections[a][0] * sections[a][1];
+        for (int64_t i = 0; i < cnt; ++i) {
+            if (outs[a][0]) outs[a][0][i] = host[off + 2 * i];
+            if (outs[a][1]) outs[a][1][i] = host[off + 2 * i + 1];
+        }
+        off += static_cast<size_t>(2 * cnt);
+    }
+    std::free(host);
+    return LTX3DROPE_OK;
+}
+
+int ltx3drope_cache_clear(void) { return cache_clear(); }
+
+int ltx3drope_can_use(const void* q_out, const void* k_out, const void* q, const void* k, int dtype, int64_t B,
+                      int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim, ltx3drope_tables_t tables,
+                      int* reason) {
+    const bool outputs = q_out != nullptr || k_out != nullptr;
+    const int r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, true, outputs);
+    if (reason) *reason = r;
+    return r == LTX3DROPE_REASON_OK ? 1 : 0;
+}
+
+int ltx3drope_kernel_choice(const void* q_out, const void* k_out, const void* q, const void* k, int dtype, int64_t B,
+                            int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
+                            ltx3drope_tables_t tables) {
+    const int r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, false);
+    if (r != LTX3DROPE_REASON_OK) return status_for_reason(r);
+    const Problem p = make_problem(const_cast<void*>(q_out), const_cast<void*>(k_out), q, k, dtype, B, T, H, W, heads,
+                                   head_dim, tables);
+    return fast_supported(p) ? static_cast<int>(Kernel::Fast) : static_cast<int>(Kernel::Plain);
+}
+
+int ltx3drope_apply_qk(void* q_out, void* k_out, const void* q, const void* k, int dtype, int64_t B, int64_t T,
+                       int64_t H, int64_t W, int64_t heads, int64_t head_dim, ltx3drope_tables_t tables,
+                       void* stream_ptr) {
+    if (tables != nullptr && tables->host) {
+        stats().rejected.fetch_add(1);
+        return LTX3DROPE_E_UNSUPPORTED;
+    }
+    const int r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, true);
+    if (r != LTX3DROPE_REASON_OK) {
+        stats().rejected.fetch_add(1);
+        return status_for_reason(r);
+    }
+    const Problem p = make_problem(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables);
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    const int device = tables->device;
+    DeviceGuard guard(device);
+
+    const int64_t path = opts().path.load();
+    if (path == 2 || !fast_supported(p)) return run_kernel(Kernel::Plain, p, stream, device);
+    if (path == 1) return run_kernel(Kernel::Fast, p, stream, device);
+
+    const int64_t gate_mode = opts().gate.load();
+    if (gate_mode == 0) return run_kernel(Kernel::Fast, p, stream, device);
+    const GateKey key{device, dtype, B, T, H, W, heads, head_dim, tables->dim_t, tables->dim_h, tables->dim_w};
+    const int state = gate_get(key);
+    if (state == LTX3DROPE_GATE_DISABLED) return run_kernel(Kernel::Plain, p, stream, device);
+    if (state == LTX3DROPE_GATE_TRUSTED && gate_mode == 1) return run_kernel(Kernel::Fast, p, stream, device);
+
+    bool equal = false;
+    const int st = verify_fast(p, stream, device, &equal);
+    if (st != LTX3DROPE_OK) return st;
+    if (equal) {
+        if (state != LTX3DROPE_GATE_TRUSTED) stats().trusted.fetch_add(1);
+        gate_set(key, LTX3DROPE_GATE_TRUSTED);
+        return LTX3DROPE_OK;
+    }
+    stats().disabled.fetch_add(1);
+    gate_set(key, LTX3DROPE_GATE_DISABLED);
+    std::fprintf(stderr,
+                 "[ltx3drope] fast kernel differs from the plain kernel for dtype=%d B=%lld T=%lld H=%lld W=%lld "
+                 "heads=%lld D=%lld; this configuration now uses the plain kernel\n",
+                 dtype, static_cast<long long>(B), static_cast<long long>(T), static_cast<long long>(H),
+                 static_cast<long long>(W), static_cast<long long>(heads), static_cast<long long>(head_dim));
+    return run_kernel(Kernel::Plain, p, stream, device);  // overwrite with the reference result
+}
+
+int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads,
+                         int64_t head_dim, int64_t dim_t, int64_t dim_h, int64_t dim_w) {
+    return gate_get(GateKey{device, dtype, B, T, H, W, heads, head_dim, dim_t, dim_h, dim_w});
+}
+
+int ltx3drope_gate_reset(void) {
+    std::lock_guard<std::mutex> lock(gate().mu);
+    gate().state.clear();
+    return LTX3DROPE_OK;
+}
+
+int ltx3drope_set_option(int option, int64_t value) {
+    switch (option) {
+        case LTX3DROPE_OPT_PATH:
+            if (value < 0 || value > 2) return LTX3DROPE_E_INVALID;
+            opts().path = value;
+            return LTX3DROPE_OK;
+        case LTX3DROPE_OPT_GATE:
+            if (value < 0 || value > 2) return LTX3DROPE_E_INVALID;
+            opts().gate = value;
+            return LTX3DROPE_OK;
+        case LTX3DROPE_OPT_FORCE_GATE_MISMATCH: opts().force_mismatch = value != 0; return LTX3DROPE_OK;
+        case LTX3DROPE_OPT_HOST_TABLES: opts().host_tables = value != 0; return LTX3DROPE_OK;
+        case LTX3DROPE_OPT_LOG: opts().log = value != 0; return LTX3DROPE_OK;
+        default: return LTX3DROPE_E_INVALID;
+    }
+}
+
+int64_t ltx3drope_get_option(int which) { return option(which); }
+
+int ltx3drope_stats(ltx3drope_stats_t* out) {
+    if (out == nullptr) return LTX3DROPE_E_INVALID;
+    cache_counters(&out->cache_hits, &out->cache_misses, &out->cache_evictions, &out->cache_live, &out->tables_alive);
+    out->gate_verifications = stats().verifications.load();
+    out->gate_trusted = stats().trusted.load();
+    out->gate_disabled = stats().disabled.load();
+    out->fast_launches = stats().fast.load();
+    out->plain_launches = stats().plain.load();
+    out->rejected = stats().rejected.load();
+    return LTX3DROPE_OK;
+}
+
+int ltx3drope_stats_reset(void) {
+    cache_counters_reset();
+    stats().verifications = 0;
+    stats().trusted = 0;
+    stats().disabled = 0;
+    stats().fast = 0;
+    stats().plain = 0;
+    stats().rejected = 0;
+    return LTX3DROPE_OK;
+}
+
+int ltx3drope_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+    if (dst == nullptr || src == nullptr || bytes < 0 || bytes % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(dst) % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0)
+        return LTX3DROPE_E_INVALID;
+    if (ranges_overlap(dst, static_cast<size_t>(bytes), src, static_cast<size_t>(bytes))) return LTX3DROPE_E_INVALID;
+    int device = 0;
+    for (const void* p : {static_cast<const void*>(dst), src}) {
+        hipPointerAttribute_t a;
+        std::memset(&a, 0, sizeof(a));
+        if (hipPointerGetAttributes(&a, p) != hipSuccess || a.type != hipMemoryTypeDevice) {
+            (void)hipGetLastError();
+            return LTX3DROPE_E_INVALID;
+        }
+        device = a.device;
+        void* base = nullptr;
+        size_t size = 0;
+        if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+            (void)hipGetLastError();
+            return LTX3DROPE_E_INVALID;
+        }
+        if (reinterpret_cast<uintptr_t>(p) + static_cast<uintptr_t>(bytes) >
+            reinterpret_cast<uintptr_t>(base) + size)
+            return LTX3DROPE_E_INVALID;
+    }
+    if (bytes == 0) return LTX3DROPE_OK;
+    DeviceGuard guard(device);
+    if (launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream), device) != hipSuccess ||
+        hipGetLastError() != hipSuccess)
+        return LTX3DROPE_E_HIP;
+    return LTX3DROPE_OK;
+}
+
+const char* ltx3drope_status_string(int status) {
+    switch (status) {
+        case LTX3DROPE_OK: return "ok";
+        case LTX3DROPE_E_INVALID: return "invalid argument";
+        case LTX3DROPE_E_UNSUPPORTED: return "unsupported input (precheck failed, nothing launched)";
+        case LTX3DROPE_E_TABLE_MISMATCH: return "tables do not match the tensors' grid or device";
+        case LTX3DROPE_E_HIP: return "HIP runtime error";
+        case LTX3DROPE_E_NOMEM: return "out of memory";
+        default: return "unknown status";
+    }
+}
+
+const char* ltx3drope_reason_string(int reason) {
+    switch (reason) {
+        case LTX3DROPE_REASON_OK: return "ok";
+        case LTX3DROPE_REASON_NULLPTR: return "null pointer or table handle";
+        case LTX3DROPE_REASON_DTYPE: return "dtype must be F32 or BF16";
+        case LTX3DROPE_REASON_NONPOSITIVE_DIM: return "every size must be positive";
+        case LTX3DROPE_REASON_SPLIT_ODD: return "each rope_dim_split entry must be even and positive";
+        case LTX3DROPE_REASON_SPLIT_SUM: return "head_dim must equal dim_t + dim_h + dim_w";
+        case LTX3DROPE_REASON_TABLE_GRID: return "tables were built for another (T, H, W) grid";
+        case LTX3DROPE_REASON_TABLE_DEVICE: return "tables live on another device";
+        case LTX3DROPE_REASON_ALIGN: return "pointers must be aligned to one (even, odd) pair";
+        case LTX3DROPE_REASON_OVERLAP: return "outputs must not overlap the inputs or each other";
+        case LTX3DROPE_REASON_TOO_LARGE: return "tensors must have fewer than 2^31 elements";
+        case LTX3DROPE_REASON_NOT_DEVICE_PTR: return "pointer is not device memory";
+        case LTX3DROPE_REASON_HOST_MODE: return "host-table test mode: nothing is launched";
+        case LTX3DROPE_REASON_EXTENT: return "a device allocation ends before the tensor does";
+        default: return "unknown reason";
+    }
+}
+
+int ltx3drope_version(void) { return LTX3DROPE_VERSION; }
+
+}  // extern "C"

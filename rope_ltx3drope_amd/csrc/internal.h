@@ -1,0 +1,69 @@
+// Internal declarations shared by the host side (tables, cache, precheck, gate)
+// and the kernel launchers of the ltx3drope library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "ltx3drope.h"
+
+// A table set: the packed per-axis (cos, sin) pairs of one grid.  Layout, in
+// float pairs: t section [T][dim_t/2], then h section [H][dim_h/2], then
+// w section [W][dim_w/2].
+struct ltx3drope_tables {
+    std::atomic<int64_t> refs{1};
+    int device = 0;
+    int64_t T = 0, H = 0, W = 0;
+    int64_t dim_t = 0, dim_h = 0, dim_w = 0;
+    double base = 0.0;
+    bool host = false;        // built in host-table test mode (malloc, never touched by HIP)
+    float* packed = nullptr;  // 2 * pairs floats (device memory unless host)
+    int64_t pairs = 0;
+};
+
+namespace ltx3drope {
+
+// Everything a kernel needs to know about one apply_qk call.  All sizes fit in
+// 32 bits because the precheck caps every tensor below 2^31 elements.
+struct Problem {
+    void* q_out;
+    void* k_out;
+    const void* q;
+    const void* k;
+    const float* tab;  // packed device tables
+    int dtype;         // LTX3DROPE_DTYPE_*
+    uint32_t B, T, H, W, heads, D;
+    uint32_t PT, PH, PW;  // pairs per head in the t, h and w chunks
+    uint32_t tab_pairs;
+};
+
+enum class Kernel { Fast = 1, Plain = 2 };
+
+// Host-side decision whether the vectorised kernel covers this problem
+// (16-B aligned pointers, 16-B head rows, chunk boundaries on vector
+// boundaries, at most 512 vectors of 16 B per token).
+bool fast_supported(const Problem& p);
+
+// Launchers (kernels.hip).  They only enqueue; the caller checks hipGetLastError.
+hipError_t launch_fast(const Problem& p, hipStream_t stream, int device);
+hipError_t launch_plain(const Problem& p, hipStream_t stream, int device);
+// Recompute with the plain kernel and count the pairs whose result differs
+// from what q_out/k_out already hold (bit patterns; two NaNs count as equal).
+hipError_t launch_verify(const Problem& p, unsigned* mismatches, hipStream_t stream, int device);
+hipError_t launch_zero_u32(unsigned* ptr, hipStream_t stream);
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream, int device);
+
+// Tables and cache (tables.cpp).
+int tables_build(int device, int64_t T, int64_t H, int64_t W, int64_t dim_t, int64_t dim_h, int64_t dim_w,
+                 double base, hipStream_t stream, ltx3drope_tables_t* out);
+int tables_release(ltx3drope_tables_t t);
+int cache_clear();
+void cache_counters(int64_t* hits, int64_t* misses, int64_t* evictions, int64_t* live, int64_t* alive);
+void cache_counters_reset();
+
+// Options (api.cpp).
+int64_t option(int which);
+
+}  // namespace ltx3drope

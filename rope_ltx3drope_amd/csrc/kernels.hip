@@ -1,0 +1,478 @@
+// HIP kernels of the fused 3D RoPE for gfx950 (MI355X), and their launchers.
+//
+// Arithmetic (sglang PR #35698 page, "Key source snippets", the CUDA kernel's
+// pair-rotation helper; "Implementation breakdown", step 2): each (even, odd)
+// pair is widened to fp32 and rotated with four separately rounded products
+// followed by one rounded difference and one rounded sum; no fused
+// multiply-add.  This file is compiled with -ffp-contract=off and the pragma
+// below, and every product/sum goes through __fmul_rn/__fsub_rn/__fadd_rn.
+// The result is cast back to the tensor dtype with round-to-nearest-even.
+//
+// Index mapping (same snippet): pair j of a head uses the t table at column j
+// for j < dim_t/2, the h table at column j - dim_t/2 for j < (dim_t+dim_h)/2,
+// and the w table for the rest; the table row is the token's t, h or w
+// coordinate, with token n = (t*H + h)*W + w in each batch element.
+//
+// Two kernels compute it:
+//  * rope_plain: one pair per thread, every index derived from the flat pair
+//    index, scalar loads and stores, integer round-to-nearest-even.  It is the
+//    reference path of the bit-exact gate and the fallback for shapes the fast
+//    kernel does not cover.  With VERIFY it recomputes the result and counts
+//    pairs that differ from what the outputs already hold.
+//  * rope_fast: one wavefront per token.  The token's (t, h, w) is decoded once
+//    per wavefront in scalar registers; each lane owns fixed 16-byte vectors of
+//    the token's heads*head_dim row, so its table column is decoded once per
+//    kernel; the tables are staged in LDS once per workgroup; Q and K move as
+//    16-byte global loads and stores; bf16 results are packed with the
+//    hardware's round-to-nearest-even conversion (v_cvt_pk_bf16_f32).
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "internal.h"
+
+#pragma clang fp contract(off)
+
+namespace ltx3drope {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kFastBlock = 256;                 // 4 wavefronts
+constexpr int kWavesPerBlock = kFastBlock / 64;
+constexpr int kPlainBlock = 256;
+constexpr uint32_t kMaxFastSlots = 8;           // 16-B vectors per lane per token (=> heads*D*s/16 <= 512)
+constexpr size_t kLdsTableBytes = 64 * 1024;    // tables larger than this are read from global memory
+
+__device__ __forceinline__ void rotate(float e, float o, float c, float s, float& ye, float& yo) {
+    const float even_cos = __fmul_rn(e, c);
+    const float odd_sin = __fmul_rn(o, s);
+    const float even_sin = __fmul_rn(e, s);
+    const float odd_cos = __fmul_rn(o, c);
+    ye = __fsub_rn(even_cos, odd_sin);
+    yo = __fadd_rn(even_sin, odd_cos);
+}
+
+// bf16 <-> fp32.  A 32-bit word holds one pair: the even element in the low half.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Integer round-to-nearest-even (plain path): add 0x7fff plus the lowest kept bit, keep the top half.
+__device__ __forceinline__ uint32_t bf16_rne_int(float y) {
+    const uint32_t u = __float_as_uint(y);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Hardware conversion of two floats to a packed bf16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t bf16_pack_hw(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    const bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ bool same_bits_or_both_nan_f32(uint32_t a, uint32_t b) {
+    return a == b || (((a & 0x7fffffffu) > 0x7f800000u) && ((b & 0x7fffffffu) > 0x7f800000u));
+}
+
+__device__ __forceinline__ bool same_bits_or_both_nan_bf16(uint32_t a, uint32_t b) {
+    return a == b || (((a & 0x7fffu) > 0x7f80u) && ((b & 0x7fffu) > 0x7f80u));
+}
+
+// ---------------------------------------------------------------------------
+// plain kernel: one pair per thread
+// ---------------------------------------------------------------------------
+
+struct PlainArgs {
+    const void* q;
+    const void* k;
+    void* q_out;
+    void* k_out;
+    const float2* tab;
+    unsigned* mismatches;
+    uint32_t pairs;  // pairs per tensor
+    uint32_t pph;    // pairs per head = D/2
+    uint32_t heads, N, HW, W;
+    uint32_t PT, PH;
+    uint32_t offH, offW;  // first pair of the h and w table sections
+    uint32_t PW;
+};
+
+template <bool BF16, bool VERIFY>
+__global__ void __launch_bounds__(kPlainBlock) rope_plain(PlainArgs a) {
+    const uint32_t stride = gridDim.x * blockDim.x;
+    uint32_t bad = 0;
+    for (uint32_t p = blockIdx.x * blockDim.x + threadIdx.x; p < a.pairs; p += stride) {
+        const uint32_t j = p % a.pph;
+        const uint32_t row = p / a.pph;      // (token, head)
+        const uint32_t token = row / a.heads;
+        const uint32_t n = token % a.N;      // position inside the batch element
+        const uint32_t t = n / a.HW;
+        const uint32_t rem = n - t * a.HW;
+        const uint32_t h = rem / a.W;
+        const uint32_t w = rem - h * a.W;
+        uint32_t idx;
+        if (j < a.PT) {
+            idx = t * a.PT + j;
+        } else if (j < a.PT + a.PH) {
+            idx = a.offH + h * a.PH + (j - a.PT);
+        } else {
+            idx = a.offW + w * a.PW + (j - a.PT - a.PH);
+        }
+        const float2 cs = a.tab[idx];
+        if constexpr (BF16) {
+            const uint32_t* src[2] = {static_cast<const uint32_t*>(a.q), static_cast<const uint32_t*>(a.k)};
+            uint32_t* dst[2] = {static_cast<uint32_t*>(a.q_out), static_cast<uint32_t*>(a.k_out)};
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const uint32_t in = src[x][p];
+                float ye, yo;
+                rotate(bf16_lo(in), bf16_hi(in), cs.x, cs.y, ye, yo);
+                const uint32_t lo = bf16_rne_int(ye), hi = bf16_rne_int(yo);
+                if constexpr (VERIFY) {
+                    const uint32_t have = dst[x][p];
+                    if (!same_bits_or_both_nan_bf16(have & 0xffffu, lo) || !same_bits_or_both_nan_bf16(have >> 16, hi))
+                        ++bad;
+                } else {
+                    dst[x][p] = lo | (hi << 16);
+                }
+            }
+        } else {
+            const float2* src[2] = {static_cast<const float2*>(a.q), static_cast<const float2*>(a.k)};
+            float2* dst[2] = {static_cast<float2*>(a.q_out), static_cast<float2*>(a.k_out)};
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const float2 in = src[x][p];
+                float ye, yo;
+                rotate(in.x, in.y, cs.x, cs.y, ye, yo);
+                if constexpr (VERIFY) {
+                    const float2 have = dst[x][p];
+                    if (!same_bits_or_both_nan_f32(__float_as_uint(have.x), __float_as_uint(ye)) ||
+                        !same_bits_or_both_nan_f32(__float_as_uint(have.y), __float_as_uint(yo)))
+                        ++bad;
+                } else {
+                    dst[x][p] = make_float2(ye, yo);
+                }
+            }
+        }
+    }
+    if constexpr (VERIFY) {
+        if (bad != 0) atomicAdd(a.mismatches, bad);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fast kernel: one wavefront per token, 16-byte vectors, tables in LDS
+// ---------------------------------------------------------------------------
+
+struct FastArgs {
+    const uint4* q;
+    const uint4* k;
+    uint4* q_out;
+    uint4* k_out;
+    const float4* tab;  // packed tables as float4 = two (cos, sin) pairs
+    uint32_t tokens;    // B*T*H*W
+    uint32_t N, HW, W;
+    uint32_t HV;        // 16-B vectors per token (heads * V)
+    uint32_t V;         // 16-B vectors per head
+    uint32_t PT, PH;    // pairs in the t and h chunks
+    uint32_t rowT4, rowH4, rowW4;  // float4 per table row of each section
+    uint32_t offH4, offW4;         // first float4 of the h and w sections
+    uint32_t tab4;                 // float4 in the packed tables
+};
+
+// PPV pairs per 16-B vector: 4 for bf16, 2 for fp32.  All chunk widths are
+// multiples of PPV pairs (checked on the host), so one vector never straddles
+// two chunks and its PPV (cos, sin) pairs are PPV/2 consecutive float4.
+template <bool BF16, int M, bool TAB_LDS>
+__global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
+    constexpr uint32_t PPV = BF16 ? 4 : 2;
+    extern __shared__ float4 lds_tab[];
+    const float4* tab = a.tab;
+    if constexpr (TAB_LDS) {
+        for (uint32_t i = threadIdx.x; i < a.tab4; i += kFastBlock) lds_tab[i] = a.tab[i];
+        __syncthreads();
+        tab = lds_tab;
+    }
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // per-lane slots: vector u = lane + 64*m of the token row, its chunk and table column
+    uint32_t sel[M], col4[M];
+    bool act[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const uint32_t u = lane + 64u * m;
+        act[m] = u < a.HV;
+        const uint32_t j0 = (u % a.V) * PPV;  // first pair of this vector inside its head
+        if (j0 < a.PT) {
+            sel[m] = 0;
+            col4[m] = j0 / 2;
+        } else if (j0 < a.PT + a.PH) {
+            sel[m] = 1;
+            col4[m] = (j0 - a.PT) / 2;
+        } else {
+            sel[m] = 2;
+            col4[m] = (j0 - a.PT - a.PH) / 2;
+        }
+    }
+
+    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
+    for (uint32_t tok = blockIdx.x * kWavesPerBlock + wave; tok < a.tokens; tok += nwaves) {
+        // token -> (t, h, w), uniform across the wavefront
+        const uint32_t n = tok % a.N;
+        const uint32_t t = n / a.HW;
+        const uint32_t rem = n - t * a.HW;
+        const uint32_t h = rem / a.W;
+        const uint32_t w = rem - h * a.W;
+        const uint32_t r0 = t * a.rowT4;
+        const uint32_t r1 = a.offH4 + h * a.rowH4;
+        const uint32_t r2 = a.offW4 + w * a.rowW4;
+        const size_t vbase = static_cast<size_t>(tok) * a.HV + lane;
+
+        uint4 qv[M], kv[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            if (act[m]) {
+                qv[m] = a.q[vbase + 64u * m];
+                kv[m] = a.k[vbase + 64u * m];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            if (!act[m]) continue;
+            const uint32_t idx = (sel[m] == 0 ? r0 : (sel[m] == 1 ? r1 : r2)) + col4[m];
+            const float4 cs0 = tab[idx];  // (c0, s0, c1, s1)
+            uint4 qo, ko;
+            if constexpr (BF16) {
+                const float4 cs1 = tab[idx + 1];  // (c2, s2, c3, s3)
+                const float c[4] = {cs0.x, cs0.z, cs1.x, cs1.z};
+                const float s[4] = {cs0.y, cs0.w, cs1.y, cs1.w};
+                const uint32_t qin[4] = {qv[m].x, qv[m].y, qv[m].z, qv[m].w};
+                const uint32_t kin[4] = {kv[m].x, kv[m].y, kv[m].z, kv[m].w};
+                uint32_t qr[4], kr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float ye, yo;
+                    rotate(bf16_lo(qin[r]), bf16_hi(qin[r]), c[r], s[r], ye, yo);
+                    qr[r] = bf16_pack_hw(ye, yo);
+                    rotate(bf16_lo(kin[r]), bf16_hi(kin[r]), c[r], s[r], ye, yo);
+                    kr[r] = bf16_pack_hw(ye, yo);
+                }
+                qo = make_uint4(qr[0], qr[1], qr[2], qr[3]);
+                ko = make_uint4(kr[0], kr[1], kr[2], kr[3]);
+            } else {
+                float y0, y1, y2, y3;
+                rotate(__uint_as_float(qv[m].x), __uint_as_float(qv[m].y), cs0.x, cs0.y, y0, y1);
+                rotate(__uint_as_float(qv[m].z), __uint_as_float(qv[m].w), cs0.z, cs0.w, y2, y3);
+                qo = make_uint4(__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3));
+                rotate(__uint_as_float(kv[m].x), __uint_as_float(kv[m].y), cs0.x, cs0.y, y0, y1);
+                rotate(__uint_as_float(kv[m].z), __uint_as_float(kv[m].w), cs0.z, cs0.w, y2, y3);
+                ko = make_uint4(__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3));
+            }
+            a.q_out[vbase + 64u * m] = qo;
+            a.k_out[vbase + 64u * m] = ko;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
+
+__global__ void zero_u32(unsigned* p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) p[0] = 0u;
+}
+
+__global__ void __launch_bounds__(256) copy16(uint4* __restrict__ dst, const uint4* __restrict__ src, size_t n) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const uint4 a0 = src[i], a1 = src[i + stride], a2 = src[i + 2 * stride], a3 = src[i + 3 * stride];
+        dst[i] = a0;
+        dst[i + stride] = a1;
+        dst[i + 2 * stride] = a2;
+        dst[i + 3 * stride] = a3;
+    }
+    for (; i < n; i += stride) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// launch geometry
+// ---------------------------------------------------------------------------
+
+std::mutex g_geo_mu;
+std::map<int, int> g_cu_count;
+std::map<std::tuple<int, const void*, size_t>, int> g_occupancy;
+
+int cu_count(int device) {
+    std::lock_guard<std::mutex> lock(g_geo_mu);
+    auto it = g_cu_count.find(device);
+    if (it != g_cu_count.end()) return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    g_cu_count[device] = n;
+    return n;
+}
+
+int blocks_per_cu(int device, const void* fn, int block, size_t lds) {
+    {
+        std::lock_guard<std::mutex> lock(g_geo_mu);
+        auto it = g_occupancy.find({device, fn, lds});
+        if (it != g_occupancy.end()) return it->second;
+    }
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, block, lds) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = 1;
+    }
+    std::lock_guard<std::mutex> lock(g_geo_mu);
+    g_occupancy[{device, fn, lds}] = n;
+    return n;
+}
+
+uint32_t elem_size(const Problem& p) { return p.dtype == LTX3DROPE_DTYPE_F32 ? 4u : 2u; }
+
+PlainArgs plain_args(const Problem& p, unsigned* mismatches) {
+    PlainArgs a;
+    a.q = p.q;
+    a.k = p.k;
+    a.q_out = p.q_out;
+    a.k_out = p.k_out;
+    a.tab = reinterpret_cast<const float2*>(p.tab);
+    a.mismatches = mismatches;
+    const uint64_t numel = uint64_t(p.B) * p.T * p.H * p.W * p.heads * p.D;
+    a.pairs = static_cast<uint32_t>(numel / 2);
+    a.pph = p.D / 2;
+    a.heads = p.heads;
+    a.N = p.T * p.H * p.W;
+    a.HW = p.H * p.W;
+    a.W = p.W;
+    a.PT = p.PT;
+    a.PH = p.PH;
+    a.PW = p.PW;
+    a.offH = p.T * p.PT;
+    a.offW = p.T * p.PT + p.H * p.PH;
+    return a;
+}
+
+template <bool VERIFY>
+hipError_t launch_plain_impl(const Problem& p, unsigned* mismatches, hipStream_t stream, int device) {
+    const PlainArgs a = plain_args(p, mismatches);
+    const uint32_t want = (a.pairs + kPlainBlock - 1) / kPlainBlock;
+    const uint32_t cap = static_cast<uint32_t>(cu_count(device)) * 32u;
+    const uint32_t blocks = want < cap ? want : cap;
+    if (blocks == 0) return hipSuccess;
+    if (p.dtype == LTX3DROPE_DTYPE_BF16)
+        hipLaunchKernelGGL((rope_plain<true, VERIFY>), dim3(blocks), dim3(kPlainBlock), 0, stream, a);
+    else
+        hipLaunchKernelGGL((rope_plain<false, VERIFY>), dim3(blocks), dim3(kPlainBlock), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <bool BF16, int M>
+hipError_t launch_fast_m(const FastArgs& a, hipStream_t stream, int device) {
+    const size_t lds = static_cast<size_t>(a.tab4) * sizeof(float4);
+    const bool in_lds = lds <= kLdsTableBytes;
+    const void* fn = in_lds ? reinterpret_cast<const void*>(&rope_fast<BF16, M, true>)
+                            : reinterpret_cast<const void*>(&rope_fast<BF16, M, false>);
+    const size_t dyn = in_lds ? lds : 0;
+    const uint32_t resident = static_cast<uint32_t>(cu_count(device) * blocks_per_cu(device, fn, kFastBlock, dyn));
+    const uint32_t want = (a.tokens + kWavesPerBlock - 1) / kWavesPerBlock;
+    const uint32_t blocks = want < resident ? want : resident;
+    if (blocks == 0) return hipSuccess;
+    if (in_lds)
+        hipLaunchKernelGGL((rope_fast<BF16, M, true>), dim3(blocks), dim3(kFastBlock), dyn, stream, a);
+    else
+        hipLaunchKernelGGL((rope_fast<BF16, M, false>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_fast_dtype(const FastArgs& a, uint32_t slots, hipStream_t stream, int device) {
+    switch (slots) {
+        case 1: return launch_fast_m<BF16, 1>(a, stream, device);
+        case 2: return launch_fast_m<BF16, 2>(a, stream, device);
+        case 3: return launch_fast_m<BF16, 3>(a, stream, device);
+        case 4: return launch_fast_m<BF16, 4>(a, stream, device);
+        case 5: return launch_fast_m<BF16, 5>(a, stream, device);
+        case 6: return launch_fast_m<BF16, 6>(a, stream, device);
+        case 7: return launch_fast_m<BF16, 7>(a, stream, device);
+        case 8: return launch_fast_m<BF16, 8>(a, stream, device);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool fast_supported(const Problem& p) {
+    const uint32_t es = elem_size(p);
+    const uint32_t ppv = 8u / es;  // pairs per 16-B vector
+    for (const void* ptr : {static_cast<const void*>(p.q), static_cast<const void*>(p.k),
+                            static_cast<const void*>(p.q_out), static_cast<const void*>(p.k_out)})
+        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return false;
+    if ((p.D * es) % 16 != 0) return false;
+    if (p.PT % ppv != 0 || p.PH % ppv != 0 || p.PW % ppv != 0) return false;
+    const uint64_t hv = uint64_t(p.heads) * (p.D * es / 16);
+    return hv >= 1 && hv <= 64ull * kMaxFastSlots;
+}
+
+hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
+    if (!fast_supported(p)) return hipErrorInvalidValue;
+    const uint32_t es = elem_size(p);
+    FastArgs a;
+    a.q = static_cast<const uint4*>(p.q);
+    a.k = static_cast<const uint4*>(p.k);
+    a.q_out = static_cast<uint4*>(p.q_out);
+    a.k_out = static_cast<uint4*>(p.k_out);
+    a.tab = reinterpret_cast<const float4*>(p.tab);
+    a.tokens = p.B * p.T * p.H * p.W;
+    a.N = p.T * p.H * p.W;
+    a.HW = p.H * p.W;
+    a.W = p.W;
+    a.V = p.D * es / 16;
+    a.HV = p.heads * a.V;
+    a.PT = p.PT;
+    a.PH = p.PH;
+    a.rowT4 = p.PT / 2;
+    a.rowH4 = p.PH / 2;
+    a.rowW4 = p.PW / 2;
+    a.offH4 = p.T * p.PT / 2;
+    a.offW4 = (p.T * p.PT + p.H * p.PH) / 2;
+    a.tab4 = p.tab_pairs / 2;
+    const uint32_t slots = (a.HV + 63) / 64;
+    return p.dtype == LTX3DROPE_DTYPE_BF16 ? launch_fast_dtype<true>(a, slots, stream, device)
+                                           : launch_fast_dtype<false>(a, slots, stream, device);
+}
+
+hipError_t launch_plain(const Problem& p, hipStream_t stream, int device) {
+    return launch_plain_impl<false>(p, nullptr, stream, device);
+}
+
+hipError_t launch_verify(const Problem& p, unsigned* mismatches, hipStream_t stream, int device) {
+    return launch_plain_impl<true>(p, mismatches, stream, device);
+}
+
+hipError_t launch_zero_u32(unsigned* ptr, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_u32, dim3(1), dim3(64), 0, stream, ptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream, int device) {
+    const size_t n = static_cast<size_t>(bytes) / 16;
+    if (n == 0) return hipSuccess;
+    const size_t want = (n + 255) / 256;
+    const size_t cap = static_cast<size_t>(cu_count(device)) * 16;
+    const uint32_t blocks = static_cast<uint32_t>(want < cap ? want : cap);
+    hipLaunchKernelGGL(copy16, dim3(blocks), dim3(256), 0, stream, static_cast<uint4*>(dst),
+                       static_cast<const uint4*>(src), n);
+    return hipGetLastError();
+}
+
+}  // namespace ltx3drope

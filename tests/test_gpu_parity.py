@@ -1,0 +1,421 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, bit for bit.
+
+Tolerance is 0 ULP for every finite value (NaN compared by class).  Small and
+ragged shapes are compared element by element in full; the full-size workloads
+are compared on sampled tokens (every head and channel of each sampled token)
+plus properties that hold at any size: fast kernel == plain kernel on the whole
+output, unit-vector readback of the tables, untouched inputs and guard bands.
+"""
+from __future__ import annotations
+
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+rla = pytest.importorskip("rope_ltx3drope_amd")
+from rope_ltx3drope_amd import _lib  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    _lib.lib()  # fails loudly if the HIP library is missing
+    yield
+
+
+@pytest.fixture(autouse=True)
+def fresh_state():
+    for opt, v in ((rla.OPT_PATH, 0), (rla.OPT_GATE, 1), (rla.OPT_FORCE_GATE_MISMATCH, 0), (rla.OPT_HOST_TABLES, 0)):
+        rla.set_option(opt, v)
+    rla.gate_reset()
+    rla.cache_clear()
+    rla.stats_reset()
+    yield
+    rla.set_option(rla.OPT_PATH, 0)
+    rla.set_option(rla.OPT_FORCE_GATE_MISMATCH, 0)
+    torch.cuda.synchronize()
+
+
+def to_dev(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == oracle.BF16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
+    if dtype == oracle.BF16:
+        return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+    return t.detach().cpu().numpy()
+
+
+def bits(x: np.ndarray) -> np.ndarray:
+    return x.view(np.uint32) if x.dtype == np.float32 else x.view(np.uint16)
+
+
+def assert_bitexact(got: np.ndarray, want: np.ndarray, dtype: str, what: str):
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    g, w = bits(got), bits(want)
+    neq = g != w
+    if neq.any():
+        gf, wf = oracle.to_f32(got, dtype), oracle.to_f32(want, dtype)
+        both_nan = np.isnan(gf) & np.isnan(wf)
+        neq &= ~both_nan
+    n = int(neq.sum())
+    if n:
+        idx = np.argwhere(neq)[:5]
+        raise AssertionError(f"{what}: {n} mismatching elements, first at {idx.tolist()}: "
+                             f"got {[hex(int(g[tuple(i)])) for i in idx]} want {[hex(int(w[tuple(i)])) for i in idx]}")
+
+
+def run(q, k, split, base=10000.0, path=0):
+    rla.set_option(rla.OPT_PATH, path)
+    with rla.tables_build(*q.shape[1:4], split, base) as tab:
+        qo, ko = rla.apply_qk(q, k, tab)
+    torch.cuda.synchronize()
+    return qo, ko
+
+
+# ---------------------------------------------------------------------------
+# full element-by-element comparisons
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wk", [1, 2])
+@pytest.mark.parametrize("path", [0, 1, 2], ids=["auto", "fast", "plain"])
+def test_small_workloads_full(wk, path):
+    w = workloads.WORKLOADS[wk]
+    log(f"workload {wk} path {path}")
+    (q, k), = workloads.generate(w)
+    want_q, want_k = oracle.rope3d_qk(q, k, w.dtype, w.split, w.base)
+    dq, dk = to_dev(q, w.dtype), to_dev(k, w.dtype)
+    qo, ko = run(dq, dk, w.split, w.base, path)
+    assert qo.data_ptr() != dq.data_ptr() and ko.data_ptr() != dk.data_ptr()
+    assert_bitexact(to_host(qo, w.dtype), want_q, w.dtype, "q")
+    assert_bitexact(to_host(ko, w.dtype), want_k, w.dtype, "k")
+    # inputs untouched
+    assert_bitexact(to_host(dq, w.dtype), q, w.dtype, "q input")
+    assert_bitexact(to_host(dk, w.dtype), k, w.dtype, "k input")
+    s = rla.stats()
+    if path == 1:
+        assert s["fast_launches"] == 1 and s["plain_launches"] == 0
+    if path == 2:
+        assert s["plain_launches"] == 1 and s["fast_launches"] == 0
+    if path == 0:
+        assert s["gate_verifications"] == 1 and s["gate_trusted"] == 1
+
+
+RAGGED = [
+    # shape, split, dtype  (fast-eligible and plain-only, ragged grids, odd heads)
+    ((1, 3, 5, 7, 3, 24), (8, 8, 8), oracle.BF16),
+    ((2, 3, 5, 7, 3, 24), (8, 8, 8), oracle.F32),
+    ((2, 1, 1, 1, 1, 6), (2, 2, 2), oracle.BF16),
+    ((1, 2, 3, 4, 5, 12), (2, 6, 4), oracle.BF16),
+    ((1, 5, 3, 2, 7, 40), (8, 16, 16), oracle.BF16),
+    ((1, 4, 9, 11, 33, 48), (16, 16, 16), oracle.BF16),
+    ((2, 2, 6, 5, 4, 96), (32, 32, 32), oracle.BF16),
+    ((1, 3, 4, 5, 2, 128), (32, 48, 48), oracle.F32),
+    ((1, 2, 3, 3, 64, 64), (16, 24, 24), oracle.BF16),
+    ((1, 2, 2, 2, 17, 16), (4, 4, 8), oracle.F32),
+    ((3, 1, 7, 1, 8, 16), (8, 4, 4), oracle.BF16),
+    ((1, 9, 1, 13, 2, 12), (4, 4, 4), oracle.F32),
+]
+
+
+@pytest.mark.parametrize("shape,split,dtype", RAGGED, ids=[f"{s}-{sp}-{d}" for s, sp, d in RAGGED])
+@pytest.mark.parametrize("path", [1, 2], ids=["fast", "plain"])
+def test_ragged_shapes_full(shape, split, dtype, path):
+    log(f"ragged {shape} {split} {dtype} path {path}")
+    q, k = workloads.generate_custom(shape, dtype, seed=sum(shape) + path)
+    want_q, want_k = oracle.rope3d_qk(q, k, dtype, split)
+    qo, ko = run(to_dev(q, dtype), to_dev(k, dtype), split, path=path)
+    assert_bitexact(to_host(qo, dtype), want_q, dtype, "q")
+    assert_bitexact(to_host(ko, dtype), want_k, dtype, "k")
+
+
+def test_misaligned_views_use_plain_kernel():
+    shape, split = (1, 3, 4, 5, 4, 32), (8, 8, 16)
+    q, k = workloads.generate_custom(shape, oracle.BF16, seed=5)
+    n = q.size
+    big = torch.empty(2 * n + 16, dtype=torch.bfloat16, device=DEV)
+    dq = big[2:2 + n].view(shape)  # 4-byte aligned, not 16-byte aligned
+    dk = big[n + 6:2 * n + 6].view(shape)
+    dq.copy_(to_dev(q, oracle.BF16))
+    dk.copy_(to_dev(k, oracle.BF16))
+    with rla.tables_build(3, 4, 5, split) as tab:
+        assert rla.kernel_choice(dq, dk, tab) == "plain"
+        qo, ko = rla.apply_qk(dq, dk, tab)
+    want_q, want_k = oracle.rope3d_qk(q, k, oracle.BF16, split)
+    assert_bitexact(to_host(qo, oracle.BF16), want_q, oracle.BF16, "q")
+    assert_bitexact(to_host(ko, oracle.BF16), want_k, oracle.BF16, "k")
+    assert rla.stats()["plain_launches"] == 1
+
+
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.F32])
+def test_special_values(dtype):
+    """Tiny (subnormal-producing), huge, zero, signed-zero, infinite and NaN inputs."""
+    shape, split = (1, 3, 4, 5, 2, 32), (8, 8, 16)
+    rng = np.random.Generator(np.random.PCG64(77))
+    vals = np.array([0.0, -0.0, 1e-38, -1e-38, 3e-39, 1e-40, 6e-45, 1e38, -3e38, 65504.0, np.inf, -np.inf, np.nan,
+                     1.0, -1.0, 0.5], dtype=np.float32)
+    x = vals[rng.integers(0, len(vals), size=2 * int(np.prod(shape)))].reshape((2,) + shape)
+    if dtype == oracle.BF16:
+        x = oracle.f32_to_bf16_bits(x)
+    q, k = x[0], x[1]
+    want_q, want_k = oracle.rope3d_qk(q, k, dtype, split)
+    for path in (1, 2):
+        qo, ko = run(to_dev(q, dtype), to_dev(k, dtype), split, path=path)
+        assert_bitexact(to_host(qo, dtype), want_q, dtype, f"q path {path}")
+        assert_bitexact(to_host(ko, dtype), want_k, dtype, f"k path {path}")
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: sampled tokens against the oracle, fast == plain in full
+# ---------------------------------------------------------------------------
+
+def sampled_check(x_host, out_dev, w, grid_index, count, seed):
+    B, T, H, W, heads, D = w.shape(grid_index)
+    ids = workloads.sample_tokens(B * T * H * W, count, seed)
+    want = oracle.rope3d_sampled(x_host, w.dtype, w.split, ids, w.base)
+    got = to_host(out_dev.view(B * T * H * W, heads, D)[torch.from_numpy(ids).to(DEV)], w.dtype)
+    assert_bitexact(got, want, w.dtype, f"workload {w.key} grid {grid_index} sampled tokens")
+
+
+def fast_equals_plain(dq, dk, qo, ko, split, base):
+    rla.set_option(rla.OPT_PATH, 2)
+    with rla.tables_build(*dq.shape[1:4], split, base) as tab:
+        pq, pk = rla.apply_qk(dq, dk, tab)
+    rla.set_option(rla.OPT_PATH, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(qo.view(torch.int16), pq.view(torch.int16))
+    assert torch.equal(ko.view(torch.int16), pk.view(torch.int16))
+
+
+def test_workload3_24_calls_one_table_set():
+    w = workloads.WORKLOADS[3]
+    log("workload 3: generating inputs")
+    (q, k), = workloads.generate(w)
+    dq, dk = to_dev(q, w.dtype), to_dev(k, w.dtype)
+    outs = []
+    for call in range(24):
+        with rla.tables_build(*w.grids[0], w.split, w.base) as tab:
+            outs.append(rla.apply_qk(dq, dk, tab))
+    torch.cuda.synchronize()
+    s = rla.stats()
+    assert (s["cache_misses"], s["cache_hits"]) == (1, 23)
+    assert s["gate_verifications"] == 1 and s["gate_trusted"] == 1 and s["fast_launches"] == 24
+    q0, k0 = outs[0]
+    for qo, ko in outs[1:]:
+        assert torch.equal(qo.view(torch.int16), q0.view(torch.int16))
+        assert torch.equal(ko.view(torch.int16), k0.view(torch.int16))
+    log("workload 3: sampled oracle comparison")
+    sampled_check(q, q0, w, 0, 3000, seed=30)
+    sampled_check(k, k0, w, 0, 3000, seed=31)
+    fast_equals_plain(dq, dk, q0, k0, w.split, w.base)
+
+
+def test_workload4_outliers():
+    w = workloads.WORKLOADS[4]
+    log("workload 4: generating inputs")
+    (q, k), = workloads.generate(w)
+    assert (oracle.to_f32(q[..., :64], w.dtype) == 60.0).any() and (oracle.to_f32(k[..., :64], w.dtype) == -60.0).any()
+    dq, dk = to_dev(q, w.dtype), to_dev(k, w.dtype)
+    qo, ko = run(dq, dk, w.split, w.base)
+    log("workload 4: sampled oracle comparison")
+    sampled_check(q, qo, w, 0, 3000, seed=40)
+    sampled_check(k, ko, w, 0, 3000, seed=41)
+    fast_equals_plain(dq, dk, qo, ko, w.split, w.base)
+
+
+def test_workload5_three_alternating_grids():
+    w = workloads.WORKLOADS[5]
+    log("workload 5: generating inputs for three grids")
+    data = workloads.generate(w)
+    dev = [(to_dev(q, w.dtype), to_dev(k, w.dtype)) for q, k in data]
+    results = {}
+    for gi in w.calls:
+        with rla.tables_build(*w.grids[gi], w.split, w.base) as tab:
+            qo, ko = rla.apply_qk(dev[gi][0], dev[gi][1], tab)
+        if gi in results:
+            torch.cuda.synchronize()
+            assert torch.equal(qo.view(torch.int16), results[gi][0].view(torch.int16))
+            assert torch.equal(ko.view(torch.int16), results[gi][1].view(torch.int16))
+        else:
+            results[gi] = (qo, ko)
+    torch.cuda.synchronize()
+    s = rla.stats()
+    assert (s["cache_misses"], s["cache_hits"], s["cache_evictions"]) == (3, 9, 0)
+    assert s["gate_verifications"] == 3 and s["gate_trusted"] == 3
+    for gi in range(3):
+        log(f"workload 5 grid {gi}: sampled oracle comparison")
+        sampled_check(data[gi][0], results[gi][0], w, gi, 1500, seed=50 + gi)
+        sampled_check(data[gi][1], results[gi][1], w, gi, 1500, seed=60 + gi)
+        fast_equals_plain(dev[gi][0], dev[gi][1], results[gi][0], results[gi][1], w.split, w.base)
+
+
+def test_unit_vectors_full_size_workload5():
+    """Pairs (1, 0) read back the bf16-rounded table row of every token, at the full size."""
+    w = workloads.WORKLOADS[5]
+    B, T, H, W, heads, D = w.shape(0)
+    tabs = oracle.grid_tables(T, H, W, w.split, w.base)
+    ct = np.concatenate([np.broadcast_to(tabs[0][0][:, None, None, :], (T, H, W, w.split[0] // 2)),
+                         np.broadcast_to(tabs[1][0][None, :, None, :], (T, H, W, w.split[1] // 2)),
+                         np.broadcast_to(tabs[2][0][None, None, :, :], (T, H, W, w.split[2] // 2))], axis=-1)
+    st = np.concatenate([np.broadcast_to(tabs[0][1][:, None, None, :], (T, H, W, w.split[0] // 2)),
+                         np.broadcast_to(tabs[1][1][None, :, None, :], (T, H, W, w.split[1] // 2)),
+                         np.broadcast_to(tabs[2][1][None, None, :, :], (T, H, W, w.split[2] // 2))], axis=-1)
+    exp_c = to_dev(oracle.f32_to_bf16_bits(ct), oracle.BF16)[None, :, :, :, None, :]
+    exp_s = to_dev(oracle.f32_to_bf16_bits(st), oracle.BF16)[None, :, :, :, None, :]
+    q = torch.zeros(w.shape(0), dtype=torch.bfloat16, device=DEV)
+    q[..., 0::2] = 1.0
+    k = torch.zeros_like(q)
+    k[..., 1::2] = 1.0
+    qo, ko = run(q, k, w.split, w.base)
+    qv = qo.view(B, T, H, W, heads, D // 2, 2)
+    kv = ko.view(B, T, H, W, heads, D // 2, 2)
+    assert torch.equal(qv[..., 0].view(torch.int16), exp_c.expand(B, T, H, W, heads, D // 2).view(torch.int16))
+    assert torch.equal(qv[..., 1].view(torch.int16), exp_s.expand(B, T, H, W, heads, D // 2).view(torch.int16))
+    # (0, 1) -> (-sin, cos); compared by value: where sin is +0 the result is 0 - 0 = +0, not -0
+    assert bool((kv[..., 0] == (-exp_s)).all())
+    assert torch.equal(kv[..., 1].view(torch.int16), exp_c.expand(B, T, H, W, heads, D // 2).view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# boundary behaviour: guard bands, gate, precheck on device pointers
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", [1, 2], ids=["fast", "plain"])
+def test_guard_bands_untouched(path):
+    shape, split = (1, 3, 4, 5, 4, 32), (8, 8, 16)
+    q, k = workloads.generate_custom(shape, oracle.BF16, seed=9)
+    n = q.size
+    guard = 4096
+    buf = torch.full((2 * n + 3 * guard,), -7.0, dtype=torch.bfloat16, device=DEV)
+    qo = buf[guard:guard + n].view(shape)
+    ko = buf[2 * guard + n:2 * guard + 2 * n].view(shape)
+    rla.set_option(rla.OPT_PATH, path)
+    with rla.tables_build(3, 4, 5, split) as tab:
+        rla.apply_qk(to_dev(q, oracle.BF16), to_dev(k, oracle.BF16), tab, qo, ko)
+    torch.cuda.synchronize()
+    for lo, hi in ((0, guard), (guard + n, 2 * guard + n), (2 * guard + 2 * n, buf.numel())):
+        assert bool((buf[lo:hi] == -7.0).all()), (lo, hi)
+    want_q, want_k = oracle.rope3d_qk(q, k, oracle.BF16, split)
+    assert_bitexact(to_host(qo, oracle.BF16), want_q, oracle.BF16, "q")
+    assert_bitexact(to_host(ko, oracle.BF16), want_k, oracle.BF16, "k")
+
+
+def test_gate_forced_mismatch_falls_back_permanently():
+    shape, split = (1, 2, 8, 8, 8, 64), (16, 24, 24)
+    q, k = workloads.generate_custom(shape, oracle.BF16, seed=3)
+    dq, dk = to_dev(q, oracle.BF16), to_dev(k, oracle.BF16)
+    want_q, want_k = oracle.rope3d_qk(q, k, oracle.BF16, split)
+    rla.set_option(rla.OPT_FORCE_GATE_MISMATCH, 1)
+    with rla.tables_build(2, 8, 8, split) as tab:
+        qo, ko = rla.apply_qk(dq, dk, tab)
+        rla.set_option(rla.OPT_FORCE_GATE_MISMATCH, 0)
+        assert rla.gate_state(0, rla.DTYPE_BF16, shape, split) == "DISABLED"
+        s = rla.stats()
+        assert s["gate_verifications"] == 1 and s["gate_disabled"] == 1
+        assert s["fast_launches"] == 1 and s["plain_launches"] == 1
+        assert_bitexact(to_host(qo, oracle.BF16), want_q, oracle.BF16, "q after fallback")
+        # later calls stay on the plain kernel, even with the forcing switched off
+        for _ in range(3):
+            qo, ko = rla.apply_qk(dq, dk, tab)
+        torch.cuda.synchronize()
+        s = rla.stats()
+        assert s["plain_launches"] == 4 and s["fast_launches"] == 1 and s["gate_verifications"] == 1
+        assert_bitexact(to_host(ko, oracle.BF16), want_k, oracle.BF16, "k on the plain path")
+    # another configuration is unaffected
+    shape2 = (2,) + shape[1:]
+    q2, k2 = workloads.generate_custom(shape2, oracle.BF16, seed=4)
+    with rla.tables_build(2, 8, 8, split) as tab:
+        rla.apply_qk(to_dev(q2, oracle.BF16), to_dev(k2, oracle.BF16), tab)
+    assert rla.gate_state(0, rla.DTYPE_BF16, shape2, split) == "TRUSTED"
+
+
+def test_gate_trusted_then_no_more_verification():
+    shape, split = (1, 2, 4, 4, 8, 64), (16, 24, 24)
+    q, k = workloads.generate_custom(shape, oracle.BF16, seed=8)
+    dq, dk = to_dev(q, oracle.BF16), to_dev(k, oracle.BF16)
+    with rla.tables_build(2, 4, 4, split) as tab:
+        for _ in range(5):
+            rla.apply_qk(dq, dk, tab)
+    torch.cuda.synchronize()
+    s = rla.stats()
+    assert s["gate_verifications"] == 1 and s["fast_launches"] == 5 and s["plain_launches"] == 0
+    assert rla.gate_state(0, rla.DTYPE_BF16, shape, split) == "TRUSTED"
+
+
+def test_precheck_on_device_pointers():
+    shape, split = (1, 2, 3, 4, 2, 12), (4, 4, 4)
+    q = torch.zeros(shape, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros_like(q)
+    with rla.tables_build(2, 3, 4, split) as tab:
+        assert rla.can_use(q, k, tab) == (True, "OK")
+        # host memory is refused
+        hq = torch.zeros(shape, dtype=torch.bfloat16).pin_memory()
+        L = _lib.lib()
+        reason = ctypes.c_int(0)
+        qo = torch.empty_like(q)
+        ko = torch.empty_like(k)
+        assert L.ltx3drope_can_use(qo.data_ptr(), ko.data_ptr(), hq.data_ptr(), k.data_ptr(), _lib.DTYPE_BF16, *shape,
+                                   tab.handle, ctypes.byref(reason)) == 0
+        assert _lib.REASONS[reason.value] == "NOT_DEVICE_PTR"
+        # a device allocation too small for the claimed shape (the 2 MiB small-block segment of torch's
+        # allocator cannot hold 115 MB); apply_qk is only called once can_use has refused, so nothing
+        # can launch on the undersized buffer
+        small = torch.empty(64, dtype=torch.bfloat16, device=DEV)
+        big_shape = (1, 2, 3, 4, 200000, 12)
+        assert L.ltx3drope_can_use(None, None, small.data_ptr(), small.data_ptr(), _lib.DTYPE_BF16, *big_shape,
+                                   tab.handle, ctypes.byref(reason)) == 0
+        assert _lib.REASONS[reason.value] == "EXTENT"
+        st = L.ltx3drope_apply_qk(qo.data_ptr(), ko.data_ptr(), small.data_ptr(), small.data_ptr(),
+                                  _lib.DTYPE_BF16, *big_shape, tab.handle, None)
+        assert st == _lib.E_UNSUPPORTED
+        # wrong grid for the tables -> table mismatch, nothing launched
+        q2 = torch.zeros((1, 2, 3, 5, 2, 12), dtype=torch.bfloat16, device=DEV)
+        with pytest.raises(rla.Ltx3dRopeUnsupported) as ei:
+            rla.apply_qk(q2, q2.clone(), tab)
+        assert ei.value.reason == "TABLE_GRID"
+        # empty tensor, unsupported dtype, non-contiguous
+        with pytest.raises(rla.Ltx3dRopeUnsupported):
+            rla.apply_qk(q[:0], k[:0], tab)
+        with pytest.raises(rla.Ltx3dRopeUnsupported):
+            rla.apply_qk(q.half(), k.half(), tab)
+        assert rla.can_use(q.transpose(1, 2), k.transpose(1, 2), tab)[0] is False
+    assert rla.stats()["fast_launches"] == 0 and rla.stats()["plain_launches"] == 0
+
+
+def test_side_stream_and_forward_pair():
+    shape, split = (1, 4, 8, 8, 16, 128), (32, 48, 48)
+    q, k = workloads.generate_custom(shape, oracle.BF16, seed=12)
+    want_q, want_k = oracle.rope3d_qk(q, k, oracle.BF16, split)
+    s = torch.cuda.Stream()
+    dq, dk = to_dev(q, oracle.BF16), to_dev(k, oracle.BF16)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        qo, ko = rla.forward_pair(dq, dk, split)
+    s.synchronize()
+    assert_bitexact(to_host(qo, oracle.BF16), want_q, oracle.BF16, "q")
+    assert_bitexact(to_host(ko, oracle.BF16), want_k, oracle.BF16, "k")
+
+
+def test_copy_helper():
+    src = torch.randint(-1000, 1000, (1 << 20,), dtype=torch.int32, device=DEV)
+    dst = torch.empty_like(src)
+    rla.copy_bytes(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
