@@ -1,0 +1,258 @@
+"""Benchmark of the fused Q+K 3D RoPE on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 5] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over one batch of synthetic,
+already-resident input: the cached table lookup (a hit after the first call),
+the precheck, and the fused rotation of Q and K into fresh outputs
+(torch.empty_like, as the decoder's wrapper does), i.e. one decoder block's
+RoPE.  The default workload is the largest bf16 one: B=2, (T, H, W) =
+(17, 68, 120), 32 heads, head_dim 96, split (32, 32, 32), N(0,1) values from
+seed 4 (6.82 GB moved per step).
+
+Printed: one JSON line.  value = algorithmic bytes per step / wall time per step
+(GB/s).  roofline.achieved = algorithmic bytes per launch / the kernel's average
+duration, measured with HIP events recorded around each launch on the stream
+the kernel runs on.  cpu_baseline = the CPU oracle timed on the host on a
+bounded slab of the same workload, scaled to the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused Q+K 3D RoPE achieved HBM GB/s (% of peak) + Gelem/s, bit-exact vs oracle"
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rope_fast.json")
+KERNEL_SOURCE = os.path.join(ROOT, "rope_ltx3drope_amd", "csrc", "kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
+    the kernel source that is built now (otherwise None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("workload") != workload_name:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--grid", type=int, default=0, help="grid index inside the workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-ceiling", action="store_true", default=True)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the fused RoPE needs no communication; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rope_ltx3drope_amd as rla
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    gi = args.grid
+    B, T, H, W, heads, D = w.shape(gi)
+    numel = w.numel(gi)
+    es = w.itemsize
+    alg_bytes = w.algorithmic_bytes(gi)  # Q and K read once, written once
+    elems = 2 * numel
+
+    t0 = time.perf_counter()
+    (q_np, k_np), = workloads.generate(w, [gi])
+    print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s: {w.name} grid {gi} "
+          f"shape {w.shape(gi)}", file=sys.stderr, flush=True)
+    tdt = torch.bfloat16 if es == 2 else torch.float32
+    if es == 2:
+        q = torch.from_numpy(q_np.view(np.int16)).view(torch.bfloat16).to(dev)
+        k = torch.from_numpy(k_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        q = torch.from_numpy(q_np).to(dev)
+        k = torch.from_numpy(k_np).to(dev)
+    assert q.dtype == tdt
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev0=None, ev1=None):
+        tab = rla.tables_build(T, H, W, w.split, w.base, device=0)
+        qo = torch.empty_like(q)
+        ko = torch.empty_like(k)
+        if ev0 is not None:
+            ev0.record(stream)
+        rla.apply_qk(q, k, tab, qo, ko)
+        if ev1 is not None:
+            ev1.record(stream)
+        tab.close()
+        return qo, ko
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = rla.stats()
+    kernel = "rope_fast" if st["fast_launches"] > 0 and st["gate_disabled"] == 0 else "rope_plain"
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        qo, ko = step(e0, e1)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    kavg_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    value = alg_bytes / (wall / args.steps) / 1e9
+    achieved = alg_bytes / kavg_s / 1e9
+    print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, kernel avg {kavg_s * 1e6:.1f} us "
+          f"(min {min(kernel_ms) * 1e3:.1f} us), {achieved:.0f} GB/s kernel", file=sys.stderr, flush=True)
+
+    # parity of the timed output on sampled tokens (the oracle computes them one by one)
+    import oracle
+
+    ids = workloads.sample_tokens(B * T * H * W, 256, seed=1234)
+    idx = torch.from_numpy(ids).to(dev)
+    mism = 0
+    for x_np, out in ((q_np, qo), (k_np, ko)):
+        want = oracle.rope3d_sampled(x_np, w.dtype, w.split, ids, w.base)
+        got = out.view(B * T * H * W, heads, D)[idx].cpu()
+        got = got.view(torch.int16).numpy().view(np.uint16) if es == 2 else got.numpy()
+        mism += int((got.view(want.dtype) != want).sum())
+
+    # copy-kernel ceiling on the same bytes (Q -> scratch, K -> scratch)
+    copy_gbs = None
+    if args.copy_ceiling:
+        a = torch.empty_like(q)
+        b = torch.empty_like(k)
+        for _ in range(3):
+            rla.copy_bytes(a, q)
+            rla.copy_bytes(b, k)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        c0.record(stream)
+        for _ in range(reps):
+            rla.copy_bytes(a, q)
+            rla.copy_bytes(b, k)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbs = alg_bytes / (c0.elapsed_time(c1) / reps / 1e3) / 1e9
+        del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, gi, q_np, k_np, args.cpu_seconds)
+
+    traffic = measured_traffic(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), inputs resident in HBM)",
+        "config": {"workload": w.name, "B": B, "grid_THW": [T, H, W], "heads": heads, "head_dim": D,
+                   "rope_dim_split": list(w.split), "base": w.base, "tokens": B * T * H * W,
+                   "algorithmic_bytes_per_step": alg_bytes, "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "gelem_per_s": round(elems / (wall / args.steps) / 1e9, 2),
+        "kernel": kernel,
+        "kernel_avg_us": round(kavg_s * 1e6, 2),
+        "copy_ceiling_GBps": None if copy_gbs is None else round(copy_gbs, 1),
+        "parity": {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    if mism:
+        sys.exit(1)
+
+
+def cpu_baseline(w, gi, q_np, k_np, target_s):
+    """The oracle, untuned, on a slab of whole t-slices of batch 0 (Q and K), single thread."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    B, T, H, W, heads, D = w.shape(gi)
+    t0 = time.perf_counter()
+    tabs = oracle.grid_tables(T, H, W, w.split, w.base)
+    t_tab = time.perf_counter() - t0
+    per_slice = 2 * H * W * heads * D
+    done = 0
+    t0 = time.perf_counter()
+    slices = 0
+    while slices < T:
+        sl = slice(slices, slices + 1)
+        oracle.rope3d(np.ascontiguousarray(q_np[0:1, sl]), w.dtype, w.split, w.base, tables=_slice_tables(tabs, slices))
+        oracle.rope3d(np.ascontiguousarray(k_np[0:1, sl]), w.dtype, w.split, w.base, tables=_slice_tables(tabs, slices))
+        done += per_slice
+        slices += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0 + t_tab
+    eps = done / dt
+    return {"value": round(eps * 2 * w.itemsize / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "gelem_per_s": round(eps / 1e9, 5), "seconds": round(dt, 2),
+            "sample": f"{slices} of {T} t-slices of batch 0 (Q and K, {done} elements) + the grid's table build, "
+                      f"numpy single thread; CPU: {_cpu_model()}"}
+
+
+def _slice_tables(tabs, t):
+    """Tables for a one-frame slab at frame t: the t table restricted to row t."""
+    (ct, st), hpair, wpair = tabs
+    return ((ct[t:t + 1], st[t:t + 1]), hpair, wpair)
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -107,8 +107,8 @@ def generate(w: Workload, grid_indices: Sequence[int] | None = None) -> List[Tup
 
     One numpy PCG64 generator seeded with the workload's seed draws, in
     order and in C order: for each grid of the workload, all of Q then all
-    of K.  Grids not requested are still drawn (to keep the stream order)
-    but dropped.  For "normal3_outliers" the values are 3*N(0,1) (an fp32
+    of K.  Grids before the last requested one are still drawn (to keep
+    the stream order) but dropped.  For "normal3_outliers" the values are 3*N(0,1) (an fp32
     multiply before the cast), then for Q and then K about 0.1 % of the
     flat positions (rng.integers, duplicates allowed) are set to +60 or -60
     with the sign drawn by rng.integers(0, 2).
@@ -116,7 +116,7 @@ def generate(w: Workload, grid_indices: Sequence[int] | None = None) -> List[Tup
     want = set(range(len(w.grids))) if grid_indices is None else set(grid_indices)
     rng = np.random.Generator(np.random.PCG64(w.seed))
     out = []
-    for gi in range(len(w.grids)):
+    for gi in range(max(want) + 1):
         n = w.numel(gi)
         scale = 3.0 if w.dist == "normal3_outliers" else None
         q = _draw_normal(rng, n, w.dtype, scale)
