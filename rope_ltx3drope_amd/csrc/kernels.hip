@@ -19,17 +19,20 @@
 //    reference path of the bit-exact gate and the fallback for shapes the fast
 //    kernel does not cover.  With VERIFY it recomputes the result and counts
 //    pairs that differ from what the outputs already hold.
-//  * rope_fast: one wavefront per token.  The token's (t, h, w) is decoded once
-//    per wavefront in scalar registers; each lane owns fixed 16-byte vectors of
-//    the token's heads*head_dim row, so its table column is decoded once per
-//    kernel; the tables are staged in LDS once per workgroup; Q and K move as
-//    16-byte global loads and stores; bf16 results are packed with the
-//    hardware's round-to-nearest-even conversion (v_cvt_pk_bf16_f32).
+//  * rope_fast: a one-shot grid in which each thread owns one 16-byte vector of
+//    Q and the same vector of K (8 bf16 or 4 fp32 values, i.e. 4 or 2 pairs).
+//    When a token's heads*head_dim row is a whole number of wavefronts, the
+//    token -> (t, h, w) decode runs once per wavefront on scalar values.  The
+//    (cos, sin) row segment of the vector comes from the packed tables with
+//    16-byte loads that stay in the L1/L2 caches (the tables are tens of KB);
+//    Q and K stream through with non-temporal 16-byte loads and stores; bf16
+//    results are packed with the hardware's round-to-nearest-even conversion
+//    (v_cvt_pk_bf16_f32).  Measured on MI355X, this shape streams faster than
+//    a persistent grid with LDS-staged tables and several vectors per lane.
 #include <hip/hip_runtime.h>
 
 #include <map>
 #include <mutex>
-#include <tuple>
 
 #include "internal.h"
 
@@ -41,11 +44,8 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kFastBlock = 256;                 // 4 wavefronts
-constexpr int kWavesPerBlock = kFastBlock / 64;
+constexpr uint32_t kFastBlock = 256;            // 4 wavefronts
 constexpr int kPlainBlock = 256;
-constexpr uint32_t kMaxFastSlots = 8;           // 16-B vectors per lane per token (=> heads*D*s/16 <= 512)
-constexpr size_t kLdsTableBytes = 64 * 1024;    // tables larger than this are read from global memory
 
 __device__ __forceinline__ void rotate(float e, float o, float c, float s, float& ye, float& yo) {
     const float even_cos = __fmul_rn(e, c);
@@ -165,118 +165,95 @@ __global__ void __launch_bounds__(kPlainBlock) rope_plain(PlainArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fast kernel: one wavefront per token, 16-byte vectors, tables in LDS
+// fast kernel: one 16-byte vector of Q and of K per thread, one-shot grid
 // ---------------------------------------------------------------------------
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 struct FastArgs {
-    const uint4* q;
-    const uint4* k;
-    uint4* q_out;
-    uint4* k_out;
-    const float4* tab;  // packed tables as float4 = two (cos, sin) pairs
-    uint32_t tokens;    // B*T*H*W
+    const u32x4* q;
+    const u32x4* k;
+    u32x4* q_out;
+    u32x4* k_out;
+    const f32x4* tab;  // packed tables as float4 = two (cos, sin) pairs
+    uint32_t total;    // 16-B vectors per tensor
+    uint32_t HV;       // 16-B vectors per token (heads * V)
+    uint32_t V;        // 16-B vectors per head
     uint32_t N, HW, W;
-    uint32_t HV;        // 16-B vectors per token (heads * V)
-    uint32_t V;         // 16-B vectors per head
-    uint32_t PT, PH;    // pairs in the t and h chunks
+    uint32_t PT, PH;   // pairs in the t and h chunks
     uint32_t rowT4, rowH4, rowW4;  // float4 per table row of each section
     uint32_t offH4, offW4;         // first float4 of the h and w sections
-    uint32_t tab4;                 // float4 in the packed tables
 };
 
-// PPV pairs per 16-B vector: 4 for bf16, 2 for fp32.  All chunk widths are
-// multiples of PPV pairs (checked on the host), so one vector never straddles
-// two chunks and its PPV (cos, sin) pairs are PPV/2 consecutive float4.
-template <bool BF16, int M, bool TAB_LDS>
+// PPV pairs per 16-B vector: 4 for bf16, 2 for fp32.  Every chunk width is a
+// multiple of PPV pairs (checked on the host), so a vector never straddles two
+// chunks and its PPV (cos, sin) pairs are PPV/2 consecutive float4 of one row.
+//
+// WAVE_TOKEN: the 16-B vectors of one token are a multiple of 64, so each
+// wavefront lies inside a single token and the token -> (t, h, w) decode is
+// done once per wavefront on wave-uniform (scalar) values.  Otherwise each lane
+// decodes its own token.
+//
+// Q and K are read and the results written with non-temporal hints: every byte
+// is touched exactly once, so the streams should not displace other data from
+// the caches (measured: +3 to +10 % on the 0.8-6.8 GB workloads).
+template <bool BF16, bool WAVE_TOKEN>
 __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
     constexpr uint32_t PPV = BF16 ? 4 : 2;
-    extern __shared__ float4 lds_tab[];
-    const float4* tab = a.tab;
-    if constexpr (TAB_LDS) {
-        for (uint32_t i = threadIdx.x; i < a.tab4; i += kFastBlock) lds_tab[i] = a.tab[i];
-        __syncthreads();
-        tab = lds_tab;
+    const uint32_t g = blockIdx.x * kFastBlock + threadIdx.x;
+    uint32_t tok, u;
+    if constexpr (WAVE_TOKEN) {
+        const uint32_t g0 = blockIdx.x * kFastBlock + __builtin_amdgcn_readfirstlane(threadIdx.x);
+        if (g0 >= a.total) return;  // whole wavefronts: total is a multiple of 64 here
+        tok = g0 / a.HV;
+        u = (g0 - tok * a.HV) + (threadIdx.x & 63u);
+    } else {
+        if (g >= a.total) return;
+        tok = g / a.HV;
+        u = g - tok * a.HV;
     }
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-    // per-lane slots: vector u = lane + 64*m of the token row, its chunk and table column
-    uint32_t sel[M], col4[M];
-    bool act[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        const uint32_t u = lane + 64u * m;
-        act[m] = u < a.HV;
-        const uint32_t j0 = (u % a.V) * PPV;  // first pair of this vector inside its head
-        if (j0 < a.PT) {
-            sel[m] = 0;
-            col4[m] = j0 / 2;
-        } else if (j0 < a.PT + a.PH) {
-            sel[m] = 1;
-            col4[m] = (j0 - a.PT) / 2;
-        } else {
-            sel[m] = 2;
-            col4[m] = (j0 - a.PT - a.PH) / 2;
-        }
+    const uint32_t n = tok % a.N;
+    const uint32_t t = n / a.HW;
+    const uint32_t rem = n - t * a.HW;
+    const uint32_t h = rem / a.W;
+    const uint32_t w = rem - h * a.W;
+    const uint32_t j0 = (u % a.V) * PPV;  // first pair of this vector inside its head
+    uint32_t idx;
+    if (j0 < a.PT) {
+        idx = t * a.rowT4 + j0 / 2;
+    } else if (j0 < a.PT + a.PH) {
+        idx = a.offH4 + h * a.rowH4 + (j0 - a.PT) / 2;
+    } else {
+        idx = a.offW4 + w * a.rowW4 + (j0 - a.PT - a.PH) / 2;
     }
-
-    const uint32_t nwaves = gridDim.x * kWavesPerBlock;
-    for (uint32_t tok = blockIdx.x * kWavesPerBlock + wave; tok < a.tokens; tok += nwaves) {
-        // token -> (t, h, w), uniform across the wavefront
-        const uint32_t n = tok % a.N;
-        const uint32_t t = n / a.HW;
-        const uint32_t rem = n - t * a.HW;
-        const uint32_t h = rem / a.W;
-        const uint32_t w = rem - h * a.W;
-        const uint32_t r0 = t * a.rowT4;
-        const uint32_t r1 = a.offH4 + h * a.rowH4;
-        const uint32_t r2 = a.offW4 + w * a.rowW4;
-        const size_t vbase = static_cast<size_t>(tok) * a.HV + lane;
-
-        uint4 qv[M], kv[M];
+    const u32x4 qv = __builtin_nontemporal_load(a.q + g);
+    const u32x4 kv = __builtin_nontemporal_load(a.k + g);
+    const f32x4 cs0 = a.tab[idx];  // (c0, s0, c1, s1)
+    u32x4 qo, ko;
+    if constexpr (BF16) {
+        const f32x4 cs1 = a.tab[idx + 1];  // (c2, s2, c3, s3)
+        const float c[4] = {cs0.x, cs0.z, cs1.x, cs1.z};
+        const float s[4] = {cs0.y, cs0.w, cs1.y, cs1.w};
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            if (act[m]) {
-                qv[m] = a.q[vbase + 64u * m];
-                kv[m] = a.k[vbase + 64u * m];
-            }
+        for (int r = 0; r < 4; ++r) {
+            float ye, yo;
+            rotate(bf16_lo(qv[r]), bf16_hi(qv[r]), c[r], s[r], ye, yo);
+            qo[r] = bf16_pack_hw(ye, yo);
+            rotate(bf16_lo(kv[r]), bf16_hi(kv[r]), c[r], s[r], ye, yo);
+            ko[r] = bf16_pack_hw(ye, yo);
         }
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            if (!act[m]) continue;
-            const uint32_t idx = (sel[m] == 0 ? r0 : (sel[m] == 1 ? r1 : r2)) + col4[m];
-            const float4 cs0 = tab[idx];  // (c0, s0, c1, s1)
-            uint4 qo, ko;
-            if constexpr (BF16) {
-                const float4 cs1 = tab[idx + 1];  // (c2, s2, c3, s3)
-                const float c[4] = {cs0.x, cs0.z, cs1.x, cs1.z};
-                const float s[4] = {cs0.y, cs0.w, cs1.y, cs1.w};
-                const uint32_t qin[4] = {qv[m].x, qv[m].y, qv[m].z, qv[m].w};
-                const uint32_t kin[4] = {kv[m].x, kv[m].y, kv[m].z, kv[m].w};
-                uint32_t qr[4], kr[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float ye, yo;
-                    rotate(bf16_lo(qin[r]), bf16_hi(qin[r]), c[r], s[r], ye, yo);
-                    qr[r] = bf16_pack_hw(ye, yo);
-                    rotate(bf16_lo(kin[r]), bf16_hi(kin[r]), c[r], s[r], ye, yo);
-                    kr[r] = bf16_pack_hw(ye, yo);
-                }
-                qo = make_uint4(qr[0], qr[1], qr[2], qr[3]);
-                ko = make_uint4(kr[0], kr[1], kr[2], kr[3]);
-            } else {
-                float y0, y1, y2, y3;
-                rotate(__uint_as_float(qv[m].x), __uint_as_float(qv[m].y), cs0.x, cs0.y, y0, y1);
-                rotate(__uint_as_float(qv[m].z), __uint_as_float(qv[m].w), cs0.z, cs0.w, y2, y3);
-                qo = make_uint4(__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3));
-                rotate(__uint_as_float(kv[m].x), __uint_as_float(kv[m].y), cs0.x, cs0.y, y0, y1);
-                rotate(__uint_as_float(kv[m].z), __uint_as_float(kv[m].w), cs0.z, cs0.w, y2, y3);
-                ko = make_uint4(__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3));
-            }
-            a.q_out[vbase + 64u * m] = qo;
-            a.k_out[vbase + 64u * m] = ko;
-        }
+    } else {
+        float y0, y1, y2, y3;
+        rotate(__uint_as_float(qv.x), __uint_as_float(qv.y), cs0.x, cs0.y, y0, y1);
+        rotate(__uint_as_float(qv.z), __uint_as_float(qv.w), cs0.z, cs0.w, y2, y3);
+        qo = (u32x4){__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
+        rotate(__uint_as_float(kv.x), __uint_as_float(kv.y), cs0.x, cs0.y, y0, y1);
+        rotate(__uint_as_float(kv.z), __uint_as_float(kv.w), cs0.z, cs0.w, y2, y3);
+        ko = (u32x4){__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
     }
+    __builtin_nontemporal_store(qo, a.q_out + g);
+    __builtin_nontemporal_store(ko, a.k_out + g);
 }
 
 // ---------------------------------------------------------------------------
@@ -306,7 +283,6 @@ __global__ void __launch_bounds__(256) copy16(uint4* __restrict__ dst, const uin
 
 std::mutex g_geo_mu;
 std::map<int, int> g_cu_count;
-std::map<std::tuple<int, const void*, size_t>, int> g_occupancy;
 
 int cu_count(int device) {
     std::lock_guard<std::mutex> lock(g_geo_mu);
@@ -318,22 +294,6 @@ int cu_count(int device) {
         n = 256;
     }
     g_cu_count[device] = n;
-    return n;
-}
-
-int blocks_per_cu(int device, const void* fn, int block, size_t lds) {
-    {
-        std::lock_guard<std::mutex> lock(g_geo_mu);
-        auto it = g_occupancy.find({device, fn, lds});
-        if (it != g_occupancy.end()) return it->second;
-    }
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, block, lds) != hipSuccess || n <= 0) {
-        (void)hipGetLastError();
-        n = 1;
-    }
-    std::lock_guard<std::mutex> lock(g_geo_mu);
-    g_occupancy[{device, fn, lds}] = n;
     return n;
 }
 
@@ -376,39 +336,6 @@ hipError_t launch_plain_impl(const Problem& p, unsigned* mismatches, hipStream_t
     return hipGetLastError();
 }
 
-template <bool BF16, int M>
-hipError_t launch_fast_m(const FastArgs& a, hipStream_t stream, int device) {
-    const size_t lds = static_cast<size_t>(a.tab4) * sizeof(float4);
-    const bool in_lds = lds <= kLdsTableBytes;
-    const void* fn = in_lds ? reinterpret_cast<const void*>(&rope_fast<BF16, M, true>)
-                            : reinterpret_cast<const void*>(&rope_fast<BF16, M, false>);
-    const size_t dyn = in_lds ? lds : 0;
-    const uint32_t resident = static_cast<uint32_t>(cu_count(device) * blocks_per_cu(device, fn, kFastBlock, dyn));
-    const uint32_t want = (a.tokens + kWavesPerBlock - 1) / kWavesPerBlock;
-    const uint32_t blocks = want < resident ? want : resident;
-    if (blocks == 0) return hipSuccess;
-    if (in_lds)
-        hipLaunchKernelGGL((rope_fast<BF16, M, true>), dim3(blocks), dim3(kFastBlock), dyn, stream, a);
-    else
-        hipLaunchKernelGGL((rope_fast<BF16, M, false>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    return hipGetLastError();
-}
-
-template <bool BF16>
-hipError_t launch_fast_dtype(const FastArgs& a, uint32_t slots, hipStream_t stream, int device) {
-    switch (slots) {
-        case 1: return launch_fast_m<BF16, 1>(a, stream, device);
-        case 2: return launch_fast_m<BF16, 2>(a, stream, device);
-        case 3: return launch_fast_m<BF16, 3>(a, stream, device);
-        case 4: return launch_fast_m<BF16, 4>(a, stream, device);
-        case 5: return launch_fast_m<BF16, 5>(a, stream, device);
-        case 6: return launch_fast_m<BF16, 6>(a, stream, device);
-        case 7: return launch_fast_m<BF16, 7>(a, stream, device);
-        case 8: return launch_fast_m<BF16, 8>(a, stream, device);
-        default: return hipErrorInvalidValue;
-    }
-}
-
 }  // namespace
 
 bool fast_supported(const Problem& p) {
@@ -418,26 +345,24 @@ bool fast_supported(const Problem& p) {
                             static_cast<const void*>(p.q_out), static_cast<const void*>(p.k_out)})
         if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return false;
     if ((p.D * es) % 16 != 0) return false;
-    if (p.PT % ppv != 0 || p.PH % ppv != 0 || p.PW % ppv != 0) return false;
-    const uint64_t hv = uint64_t(p.heads) * (p.D * es / 16);
-    return hv >= 1 && hv <= 64ull * kMaxFastSlots;
+    return p.PT % ppv == 0 && p.PH % ppv == 0 && p.PW % ppv == 0;
 }
 
 hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
     if (!fast_supported(p)) return hipErrorInvalidValue;
     const uint32_t es = elem_size(p);
     FastArgs a;
-    a.q = static_cast<const uint4*>(p.q);
-    a.k = static_cast<const uint4*>(p.k);
-    a.q_out = static_cast<uint4*>(p.q_out);
-    a.k_out = static_cast<uint4*>(p.k_out);
-    a.tab = reinterpret_cast<const float4*>(p.tab);
-    a.tokens = p.B * p.T * p.H * p.W;
+    a.q = static_cast<const u32x4*>(p.q);
+    a.k = static_cast<const u32x4*>(p.k);
+    a.q_out = static_cast<u32x4*>(p.q_out);
+    a.k_out = static_cast<u32x4*>(p.k_out);
+    a.tab = reinterpret_cast<const f32x4*>(p.tab);
+    a.V = p.D * es / 16;
+    a.HV = p.heads * a.V;
+    a.total = p.B * p.T * p.H * p.W * a.HV;
     a.N = p.T * p.H * p.W;
     a.HW = p.H * p.W;
     a.W = p.W;
-    a.V = p.D * es / 16;
-    a.HV = p.heads * a.V;
     a.PT = p.PT;
     a.PH = p.PH;
     a.rowT4 = p.PT / 2;
@@ -445,10 +370,20 @@ hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
     a.rowW4 = p.PW / 2;
     a.offH4 = p.T * p.PT / 2;
     a.offW4 = (p.T * p.PT + p.H * p.PH) / 2;
-    a.tab4 = p.tab_pairs / 2;
-    const uint32_t slots = (a.HV + 63) / 64;
-    return p.dtype == LTX3DROPE_DTYPE_BF16 ? launch_fast_dtype<true>(a, slots, stream, device)
-                                           : launch_fast_dtype<false>(a, slots, stream, device);
+    const uint32_t blocks = (a.total + kFastBlock - 1) / kFastBlock;
+    if (blocks == 0) return hipSuccess;
+    const bool wave_token = a.HV % 64 == 0;
+    const bool bf16 = p.dtype == LTX3DROPE_DTYPE_BF16;
+    (void)device;
+    if (bf16 && wave_token)
+        hipLaunchKernelGGL((rope_fast<true, true>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    else if (bf16)
+        hipLaunchKernelGGL((rope_fast<true, false>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    else if (wave_token)
+        hipLaunchKernelGGL((rope_fast<false, true>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    else
+        hipLaunchKernelGGL((rope_fast<false, false>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_plain(const Problem& p, hipStream_t stream, int device) {

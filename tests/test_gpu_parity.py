@@ -132,6 +132,9 @@ RAGGED = [
     ((1, 2, 2, 2, 17, 16), (4, 4, 8), oracle.F32),
     ((3, 1, 7, 1, 8, 16), (8, 4, 4), oracle.BF16),
     ((1, 9, 1, 13, 2, 12), (4, 4, 4), oracle.F32),
+    ((1, 2, 3, 4, 40, 128), (32, 48, 48), oracle.BF16),   # 640 vectors per token
+    ((1, 2, 2, 3, 80, 96), (32, 32, 32), oracle.BF16),    # 960 vectors per token
+    ((1, 1, 2, 2, 3, 20), (8, 8, 4), oracle.BF16),        # head row not a whole 16-byte vector
 ]
 
 

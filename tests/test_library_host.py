@@ -338,9 +338,12 @@ def test_kernel_choice_rules():
         assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_BF16, *shp, tab.handle) == 1
         # 4-byte aligned but not 16-byte aligned -> plain
         assert L.ltx3drope_kernel_choice(qo, ko, q + 4, k, _lib.DTYPE_BF16, *shp, tab.handle) == 2
-        # more than 512 16-byte vectors per token -> plain
+        # many heads (640 16-byte vectors per token) stay on the fast kernel
         shp_big = (1, 2, 3, 4, 40, 128)
-        assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_BF16, *shp_big, tab.handle) == 2
+        assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_BF16, *shp_big, tab.handle) == 1
+        # head rows that are not a whole number of 16-byte vectors -> plain
+        with rla.tables_build(2, 3, 4, (8, 8, 4)) as tab2:
+            assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_BF16, 1, 2, 3, 4, 3, 20, tab2.handle) == 2
     with rla.tables_build(2, 3, 4, (2, 6, 4)) as tab:  # chunk widths not multiples of 4 pairs
         assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_BF16, 1, 2, 3, 4, 2, 12, tab.handle) == 2
     with rla.tables_build(2, 3, 4, (4, 8, 4)) as tab:  # fp32: 2 pairs per vector
