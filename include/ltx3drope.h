@@ -210,8 +210,10 @@ int ltx3drope_kernel_choice(const void* q_out, const void* k_out, const void* q,
                             int dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads,
                             int64_t head_dim, ltx3drope_tables_t tables);
 
-/* Measurement helper: copy `bytes` (a multiple of 16, both pointers 16-B aligned) from src to dst
-   with a plain streaming kernel on `stream`; used to calibrate bandwidth and traffic counters. */
+/* Measurement helper: copy `bytes` (a multiple of 16, fewer than 2^32 - 64 vectors of 16 B, both
+   pointers 16-B aligned, non-overlapping device memory) from src to dst with a plain streaming kernel
+   on `stream` (the fast kernel's launch shape and cache hints, one read and one write stream); used
+   as the bandwidth ceiling and to calibrate traffic counters.  E_INVALID on bad arguments, E_HIP. */
 int ltx3drope_copy(void* dst, const void* src, int64_t bytes, void* stream);
 
 const char* ltx3drope_status_string(int status);

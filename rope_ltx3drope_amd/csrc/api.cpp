@@ -453,6 +453,7 @@ int ltx3drope_copy(void* dst, const void* src, int64_t bytes, void* stream) {
         reinterpret_cast<uintptr_t>(dst) % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0)
         return LTX3DROPE_E_INVALID;
     if (ranges_overlap(dst, static_cast<size_t>(bytes), src, static_cast<size_t>(bytes))) return LTX3DROPE_E_INVALID;
+    if (bytes / 16 >= (int64_t(1) << 32) - 64) return LTX3DROPE_E_INVALID;
     int device = 0;
     for (const void* p : {static_cast<const void*>(dst), src}) {
         hipPointerAttribute_t a;

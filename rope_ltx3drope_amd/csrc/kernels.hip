@@ -44,7 +44,7 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr uint32_t kFastBlock = 256;            // 4 wavefronts
+constexpr uint32_t kFastBlock = 64;             // one wavefront per workgroup
 constexpr int kPlainBlock = 256;
 
 __device__ __forceinline__ void rotate(float e, float o, float c, float s, float& ye, float& yo) {
@@ -190,9 +190,16 @@ struct FastArgs {
 // multiple of PPV pairs (checked on the host), so a vector never straddles two
 // chunks and its PPV (cos, sin) pairs are PPV/2 consecutive float4 of one row.
 //
-// WAVE_TOKEN: the 16-B vectors of one token are a multiple of 64, so each
-// wavefront lies inside a single token and the token -> (t, h, w) decode is
-// done once per wavefront on wave-uniform (scalar) values.  Otherwise each lane
+// Grid: 2 * ceil(vectors / 64) workgroups of one wavefront.  The first half of
+// the grid rotates Q, the second half K, so that while the grid runs the memory
+// system mostly sees one read stream and one write stream rather than four
+// (measured on MI355X: 6.6 TB/s against 6.0 TB/s when every thread handles the
+// same vector of Q and of K; one-wavefront workgroups beat 128-1024 threads).
+// Both halves are one launch.
+//
+// WAVE_TOKEN: a token's heads*head_dim row is a whole number of wavefronts, so
+// each wavefront lies inside one token and the token -> (t, h, w) decode runs
+// once per wavefront on wave-uniform (scalar) values.  Otherwise each lane
 // decodes its own token.
 //
 // Q and K are read and the results written with non-temporal hints: every byte
@@ -201,13 +208,18 @@ struct FastArgs {
 template <bool BF16, bool WAVE_TOKEN>
 __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
     constexpr uint32_t PPV = BF16 ? 4 : 2;
-    const uint32_t g = blockIdx.x * kFastBlock + threadIdx.x;
+    const uint32_t half = gridDim.x >> 1;
+    const bool second = blockIdx.x >= half;  // wave-uniform
+    const uint32_t blk = second ? blockIdx.x - half : blockIdx.x;
+    const u32x4* __restrict__ src = second ? a.k : a.q;
+    u32x4* __restrict__ dst = second ? a.k_out : a.q_out;
+    const uint32_t g = blk * kFastBlock + threadIdx.x;
     uint32_t tok, u;
     if constexpr (WAVE_TOKEN) {
-        const uint32_t g0 = blockIdx.x * kFastBlock + __builtin_amdgcn_readfirstlane(threadIdx.x);
+        const uint32_t g0 = blk * kFastBlock;
         if (g0 >= a.total) return;  // whole wavefronts: total is a multiple of 64 here
         tok = g0 / a.HV;
-        u = (g0 - tok * a.HV) + (threadIdx.x & 63u);
+        u = (g0 - tok * a.HV) + threadIdx.x;
     } else {
         if (g >= a.total) return;
         tok = g / a.HV;
@@ -227,10 +239,9 @@ __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
     } else {
         idx = a.offW4 + w * a.rowW4 + (j0 - a.PT - a.PH) / 2;
     }
-    const u32x4 qv = __builtin_nontemporal_load(a.q + g);
-    const u32x4 kv = __builtin_nontemporal_load(a.k + g);
+    const u32x4 x = __builtin_nontemporal_load(src + g);
     const f32x4 cs0 = a.tab[idx];  // (c0, s0, c1, s1)
-    u32x4 qo, ko;
+    u32x4 y;
     if constexpr (BF16) {
         const f32x4 cs1 = a.tab[idx + 1];  // (c2, s2, c3, s3)
         const float c[4] = {cs0.x, cs0.z, cs1.x, cs1.z};
@@ -238,22 +249,16 @@ __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float ye, yo;
-            rotate(bf16_lo(qv[r]), bf16_hi(qv[r]), c[r], s[r], ye, yo);
-            qo[r] = bf16_pack_hw(ye, yo);
-            rotate(bf16_lo(kv[r]), bf16_hi(kv[r]), c[r], s[r], ye, yo);
-            ko[r] = bf16_pack_hw(ye, yo);
+            rotate(bf16_lo(x[r]), bf16_hi(x[r]), c[r], s[r], ye, yo);
+            y[r] = bf16_pack_hw(ye, yo);
         }
     } else {
         float y0, y1, y2, y3;
-        rotate(__uint_as_float(qv.x), __uint_as_float(qv.y), cs0.x, cs0.y, y0, y1);
-        rotate(__uint_as_float(qv.z), __uint_as_float(qv.w), cs0.z, cs0.w, y2, y3);
-        qo = (u32x4){__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
-        rotate(__uint_as_float(kv.x), __uint_as_float(kv.y), cs0.x, cs0.y, y0, y1);
-        rotate(__uint_as_float(kv.z), __uint_as_float(kv.w), cs0.z, cs0.w, y2, y3);
-        ko = (u32x4){__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
+        rotate(__uint_as_float(x.x), __uint_as_float(x.y), cs0.x, cs0.y, y0, y1);
+        rotate(__uint_as_float(x.z), __uint_as_float(x.w), cs0.z, cs0.w, y2, y3);
+        y = (u32x4){__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
     }
-    __builtin_nontemporal_store(qo, a.q_out + g);
-    __builtin_nontemporal_store(ko, a.k_out + g);
+    __builtin_nontemporal_store(y, dst + g);
 }
 
 // ---------------------------------------------------------------------------
@@ -264,17 +269,11 @@ __global__ void zero_u32(unsigned* p) {
     if (threadIdx.x == 0 && blockIdx.x == 0) p[0] = 0u;
 }
 
-__global__ void __launch_bounds__(256) copy16(uint4* __restrict__ dst, const uint4* __restrict__ src, size_t n) {
-    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n; i += 4 * stride) {
-        const uint4 a0 = src[i], a1 = src[i + stride], a2 = src[i + 2 * stride], a3 = src[i + 3 * stride];
-        dst[i] = a0;
-        dst[i + stride] = a1;
-        dst[i + 2 * stride] = a2;
-        dst[i + 3 * stride] = a3;
-    }
-    for (; i < n; i += stride) dst[i] = src[i];
+// Bandwidth reference: the same launch shape and cache hints as rope_fast, one
+// read stream and one write stream.
+__global__ void __launch_bounds__(kFastBlock) copy16(u32x4* __restrict__ dst, const u32x4* __restrict__ src, uint32_t n) {
+    const uint32_t i = blockIdx.x * kFastBlock + threadIdx.x;
+    if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 // ---------------------------------------------------------------------------
@@ -370,8 +369,9 @@ hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
     a.rowW4 = p.PW / 2;
     a.offH4 = p.T * p.PT / 2;
     a.offW4 = (p.T * p.PT + p.H * p.PH) / 2;
-    const uint32_t blocks = (a.total + kFastBlock - 1) / kFastBlock;
-    if (blocks == 0) return hipSuccess;
+    const uint32_t per_tensor = (a.total + kFastBlock - 1) / kFastBlock;
+    if (per_tensor == 0) return hipSuccess;
+    const uint32_t blocks = 2 * per_tensor;  // first half Q, second half K
     const bool wave_token = a.HV % 64 == 0;
     const bool bf16 = p.dtype == LTX3DROPE_DTYPE_BF16;
     (void)device;
@@ -400,13 +400,13 @@ hipError_t launch_zero_u32(unsigned* ptr, hipStream_t stream) {
 }
 
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream, int device) {
-    const size_t n = static_cast<size_t>(bytes) / 16;
+    (void)device;
+    const uint64_t n = static_cast<uint64_t>(bytes) / 16;
     if (n == 0) return hipSuccess;
-    const size_t want = (n + 255) / 256;
-    const size_t cap = static_cast<size_t>(cu_count(device)) * 16;
-    const uint32_t blocks = static_cast<uint32_t>(want < cap ? want : cap);
-    hipLaunchKernelGGL(copy16, dim3(blocks), dim3(256), 0, stream, static_cast<uint4*>(dst),
-                       static_cast<const uint4*>(src), n);
+    if (n > 0xffffffffull - kFastBlock) return hipErrorInvalidValue;
+    const uint32_t blocks = static_cast<uint32_t>((n + kFastBlock - 1) / kFastBlock);
+    hipLaunchKernelGGL(copy16, dim3(blocks), dim3(kFastBlock), 0, stream, static_cast<u32x4*>(dst),
+                       static_cast<const u32x4*>(src), static_cast<uint32_t>(n));
     return hipGetLastError();
 }
 
