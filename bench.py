@@ -218,7 +218,8 @@ def main():
 
 
 def cpu_baseline(w, gi, q_np, k_np, target_s):
-    """The oracle, untuned, on a slab of whole t-slices of batch 0 (Q and K), single thread."""
+    """The oracle, untuned, on whole (batch, frame) slabs of the same inputs (Q and K), single thread,
+    until about target_s seconds of CPU work are done."""
     import numpy as np
 
     import oracle
@@ -231,24 +232,25 @@ def cpu_baseline(w, gi, q_np, k_np, target_s):
     t0 = time.perf_counter()
     tabs = oracle.grid_tables(T, H, W, w.split, w.base)
     t_tab = time.perf_counter() - t0
-    per_slice = 2 * H * W * heads * D
+    per_slab = 2 * H * W * heads * D
     done = 0
+    slabs = 0
     t0 = time.perf_counter()
-    slices = 0
-    while slices < T:
-        sl = slice(slices, slices + 1)
-        oracle.rope3d(np.ascontiguousarray(q_np[0:1, sl]), w.dtype, w.split, w.base, tables=_slice_tables(tabs, slices))
-        oracle.rope3d(np.ascontiguousarray(k_np[0:1, sl]), w.dtype, w.split, w.base, tables=_slice_tables(tabs, slices))
-        done += per_slice
-        slices += 1
+    while slabs < B * T:
+        b, t = divmod(slabs, T)
+        for x in (q_np, k_np):
+            oracle.rope3d(np.ascontiguousarray(x[b:b + 1, t:t + 1]), w.dtype, w.split, w.base,
+                          tables=_slice_tables(tabs, t))
+        done += per_slab
+        slabs += 1
         if time.perf_counter() - t0 >= target_s:
             break
     dt = time.perf_counter() - t0 + t_tab
     eps = done / dt
     return {"value": round(eps * 2 * w.itemsize / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "gelem_per_s": round(eps / 1e9, 5), "seconds": round(dt, 2),
-            "sample": f"{slices} of {T} t-slices of batch 0 (Q and K, {done} elements) + the grid's table build, "
-                      f"numpy single thread; CPU: {_cpu_model()}"}
+            "sample": f"{slabs} of {B * T} (batch, frame) slabs, Q and K ({done} elements), plus the grid's "
+                      f"table build; numpy, one thread pinned to one core; CPU: {_cpu_model()}"}
 
 
 def _slice_tables(tabs, t):
