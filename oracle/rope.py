@@ -119,11 +119,12 @@ def rotate_pairs(even: np.ndarray, odd: np.ndarray, cos: np.ndarray, sin: np.nda
     rounded sum.  Separate numpy ufunc calls cannot fuse into an FMA.
     """
     f = np.float32
-    even_cos = np.multiply(even, cos, dtype=f)
-    odd_sin = np.multiply(odd, sin, dtype=f)
-    even_sin = np.multiply(even, sin, dtype=f)
-    odd_cos = np.multiply(odd, cos, dtype=f)
-    return np.subtract(even_cos, odd_sin, dtype=f), np.add(even_sin, odd_cos, dtype=f)
+    with np.errstate(over="ignore", invalid="ignore"):
+        even_cos = np.multiply(even, cos, dtype=f)
+        odd_sin = np.multiply(odd, sin, dtype=f)
+        even_sin = np.multiply(even, sin, dtype=f)
+        odd_cos = np.multiply(odd, cos, dtype=f)
+        return np.subtract(even_cos, odd_sin, dtype=f), np.add(even_sin, odd_cos, dtype=f)
 
 
 def validate(shape: Sequence[int], split: Sequence[int]) -> None:
@@ -171,47 +172,67 @@ def token_coords(token_ids: np.ndarray, T: int, H: int, W: int):
 
 
 def rope3d(x: np.ndarray, dtype: str, split: Sequence[int], base: float = 10000.0,
-           tables: Tables | None = None) -> np.ndarray:
+           tables: Tables | None = None, offsets: Sequence[int] = (0, 0, 0),
+           grid: Sequence[int] | None = None) -> np.ndarray:
     """Rotate one [B, T, H, W, heads, D] tensor; returns a new array of the same dtype.
+
+    offsets / grid: the tensor may be a shard of a larger (T_g, H_g, W_g) grid
+    (the frames, rows and columns [offset, offset + size) of each axis); a
+    token then takes the table rows of its global coordinate, i.e. its local
+    coordinate plus the axis offset.  By default the tensor is the whole grid.
 
     Processed one (b, t) slab at a time to bound host memory; every slab is
     an independent application of apply_rope_tokens.
     """
     validate(x.shape, split)
     B, T, H, W, heads, D = x.shape
+    t0, h0, w0 = (int(o) for o in offsets)
+    Tg, Hg, Wg = grid if grid is not None else (T + t0, H + h0, W + w0)
+    if min(t0, h0, w0) < 0 or t0 + T > Tg or h0 + H > Hg or w0 + W > Wg:
+        raise ValueError("the shard does not lie inside the grid")
     if tables is None:
-        tables = grid_tables(T, H, W, split, base)
+        tables = grid_tables(Tg, Hg, Wg, split, base)
     out = np.empty_like(x)
-    hh, ww = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+    hh, ww = np.meshgrid(np.arange(H) + h0, np.arange(W) + w0, indexing="ij")
     hh = hh.reshape(-1)
     ww = ww.reshape(-1)
     for b in range(B):
         for t in range(T):
-            tt = np.full(H * W, t, dtype=np.int64)
+            tt = np.full(H * W, t + t0, dtype=np.int64)
             slab = x[b, t].reshape(H * W, heads, D)
             out[b, t] = apply_rope_tokens(slab, dtype, (tt, hh, ww), tables, split).reshape(H, W, heads, D)
     return out
 
 
 def rope3d_qk(q: np.ndarray, k: np.ndarray, dtype: str, split: Sequence[int], base: float = 10000.0,
-              tables: Tables | None = None):
+              tables: Tables | None = None, offsets: Sequence[int] = (0, 0, 0),
+              grid: Sequence[int] | None = None):
     """(q_out, k_out): both tensors rotated with one shared table set."""
     if q.shape != k.shape:
         raise ValueError("q and k must have the same shape")
     validate(q.shape, split)
     B, T, H, W, heads, D = q.shape
+    if grid is None:
+        grid = (T + offsets[0], H + offsets[1], W + offsets[2])
     if tables is None:
-        tables = grid_tables(T, H, W, split, base)
-    return rope3d(q, dtype, split, base, tables), rope3d(k, dtype, split, base, tables)
+        tables = grid_tables(*grid, split, base)
+    return (rope3d(q, dtype, split, base, tables, offsets, grid),
+            rope3d(k, dtype, split, base, tables, offsets, grid))
 
 
 def rope3d_sampled(x: np.ndarray, dtype: str, split: Sequence[int], token_ids: np.ndarray,
-                   base: float = 10000.0, tables: Tables | None = None) -> np.ndarray:
-    """Rotated rows [len(token_ids), heads, D] for selected flat token indices of x."""
+                   base: float = 10000.0, tables: Tables | None = None, offsets: Sequence[int] = (0, 0, 0),
+                   grid: Sequence[int] | None = None) -> np.ndarray:
+    """Rotated rows [len(token_ids), heads, D] for selected flat token indices of x
+    (x may be a shard of a larger grid, as in rope3d)."""
     validate(x.shape, split)
     B, T, H, W, heads, D = x.shape
+    if grid is None:
+        grid = (T + offsets[0], H + offsets[1], W + offsets[2])
     if tables is None:
-        tables = grid_tables(T, H, W, split, base)
+        tables = grid_tables(*grid, split, base)
     ids = np.asarray(token_ids, dtype=np.int64)
     rows = x.reshape(B * T * H * W, heads, D)[ids]
-    return apply_rope_tokens(rows, dtype, token_coords(ids, T, H, W), tables, split)
+    t, h, w = token_coords(ids, T, H, W)
+    coords = (t + offsets[0], h + offsets[1], w + offsets[2])
+    return apply_rope_tokens(rows, dtype, coords, tables, split)

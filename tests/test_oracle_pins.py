@@ -77,12 +77,15 @@ def pin_table_closed_forms(length, dim, base=BASE):
     assert np.all(np.abs(r - 1.0) <= 2.0 ** -22), np.max(np.abs(r - 1.0))
 
 
-def _brute_force_qk(q, k, dtype, split, base):
+def _brute_force_qk(q, k, dtype, split, base, offsets=(0, 0, 0)):
     """Element-by-element rotation through explicit strides, with the tables taken
-    from the arbitrary-precision evaluation and bf16 rounding from torch."""
+    from the arbitrary-precision evaluation and bf16 rounding from torch.  With
+    offsets the tensor is a shard whose first frame/row/column sits at those
+    global coordinates."""
     B, T, H, W, heads, D = q.shape
     dt, dh, dw = split
-    tabs = [exact_trig.exact_axis_tables(L, d, base) for L, d in ((T, dt), (H, dh), (W, dw))]
+    t0, h0, w0 = offsets
+    tabs = [exact_trig.exact_axis_tables(L, d, base) for L, d in ((T + t0, dt), (H + h0, dh), (W + w0, dw))]
     for _, _, amb in tabs:
         assert not amb.any()
     outs = []
@@ -97,11 +100,11 @@ def _brute_force_qk(q, k, dtype, split, base):
                             row = ((((b * T + t) * H + h) * W + w) * heads + hd) * D
                             for j in range(D // 2):
                                 if j < dt // 2:
-                                    axis, col, pos = 0, j, t
+                                    axis, col, pos = 0, j, t + t0
                                 elif j < (dt + dh) // 2:
-                                    axis, col, pos = 1, j - dt // 2, h
+                                    axis, col, pos = 1, j - dt // 2, h + h0
                                 else:
-                                    axis, col, pos = 2, j - (dt + dh) // 2, w
+                                    axis, col, pos = 2, j - (dt + dh) // 2, w + w0
                                 c = tabs[axis][0][pos, col]
                                 s = tabs[axis][1][pos, col]
                                 if dtype == oracle.BF16:
@@ -120,10 +123,10 @@ def _brute_force_qk(q, k, dtype, split, base):
     return outs
 
 
-def pin_brute_force(shape, dtype, split, seed, base=BASE):
+def pin_brute_force(shape, dtype, split, seed, base=BASE, offsets=(0, 0, 0)):
     q, k = workloads.generate_custom(shape, dtype, seed)
-    qo, ko = orc.rope3d_qk(q, k, dtype, split, base)
-    bq, bk = _brute_force_qk(q, k, dtype, split, base)
+    qo, ko = orc.rope3d_qk(q, k, dtype, split, base, offsets=offsets)
+    bq, bk = _brute_force_qk(q, k, dtype, split, base, offsets)
     assert qo.dtype == q.dtype and ko.dtype == k.dtype
     np.testing.assert_array_equal(qo.view(np.uint32 if dtype == oracle.F32 else np.uint16),
                                   bq.view(np.uint32 if dtype == oracle.F32 else np.uint16))
@@ -219,6 +222,22 @@ def pin_complex_product_bound(seed=14):
     assert np.all(np.abs(qo[..., 1::2] - exact.imag) <= bound_im)
 
 
+def pin_shard_is_slab_of_full(full_shape, split, offsets, local, seed):
+    """Rotating a slab of a tensor as a shard (with its offsets into the full grid) gives
+    exactly that slab of the full tensor's result."""
+    q, k = workloads.generate_custom(full_shape, oracle.BF16, seed)
+    fq, fk = orc.rope3d_qk(q, k, oracle.BF16, split)
+    (t0, h0, w0), (tl, hl, wl) = offsets, local
+    sl = (slice(None), slice(t0, t0 + tl), slice(h0, h0 + hl), slice(w0, w0 + wl))
+    sq, sk = np.ascontiguousarray(q[sl]), np.ascontiguousarray(k[sl])
+    oq, ok = orc.rope3d_qk(sq, sk, oracle.BF16, split, offsets=offsets, grid=full_shape[1:4])
+    np.testing.assert_array_equal(oq, fq[sl])
+    np.testing.assert_array_equal(ok, fk[sl])
+    ids = np.array([0, 3, sq.shape[0] * tl * hl * wl - 1])
+    np.testing.assert_array_equal(orc.rope3d_sampled(sq, oracle.BF16, split, ids, offsets=offsets, grid=full_shape[1:4]),
+                                  oq.reshape(-1, *sq.shape[4:])[ids])
+
+
 def pin_sampled_equals_full(seed=15):
     shape = (2, 3, 4, 5, 2, 24)
     split = (8, 8, 8)
@@ -266,6 +285,8 @@ ALL_PINS = [
     ("brute_f32", lambda: pin_brute_force((1, 2, 3, 2, 2, 16), oracle.F32, (4, 8, 4), 21)),
     ("brute_bf16", lambda: pin_brute_force((2, 2, 2, 3, 1, 12), oracle.BF16, (4, 4, 4), 22)),
     ("bf16_cast", pin_bf16_cast),
+    ("brute_shard", lambda: pin_brute_force((1, 2, 2, 3, 1, 12), oracle.BF16, (4, 4, 4), 25, offsets=(3, 1, 2))),
+    ("shard_slab", lambda: pin_shard_is_slab_of_full((2, 6, 5, 7, 2, 24), (8, 8, 8), (2, 1, 3), (3, 3, 4), 26)),
 ]
 
 
@@ -348,6 +369,27 @@ def test_brute_force_tiny_grids(shape, dtype, split, seed):
 
 def test_sampled_equals_full():
     pin_sampled_equals_full()
+
+
+@pytest.mark.parametrize("shape,dtype,split,offsets", [
+    ((1, 2, 2, 3, 1, 12), oracle.BF16, (4, 4, 4), (3, 1, 2)),
+    ((2, 1, 3, 2, 2, 16), oracle.F32, (4, 8, 4), (5, 0, 7)),
+])
+def test_brute_force_shards(shape, dtype, split, offsets):
+    pin_brute_force(shape, dtype, split, 27, offsets=offsets)
+
+
+def test_shard_is_slab_of_full():
+    pin_shard_is_slab_of_full((2, 6, 5, 7, 2, 24), (8, 8, 8), (2, 1, 3), (3, 3, 4), 26)
+    pin_shard_is_slab_of_full((1, 4, 4, 4, 3, 32), (8, 8, 16), (0, 2, 0), (4, 2, 4), 28)
+
+
+def test_shard_outside_grid_rejected():
+    q, k = workloads.generate_custom((1, 2, 2, 2, 1, 12), oracle.BF16, 1)
+    with pytest.raises(ValueError):
+        orc.rope3d(q, oracle.BF16, (4, 4, 4), offsets=(1, 0, 0), grid=(2, 2, 2))
+    with pytest.raises(ValueError):
+        orc.rope3d(q, oracle.BF16, (4, 4, 4), offsets=(-1, 0, 0))
 
 
 def test_bf16_cast_against_torch_and_closed_forms():
@@ -435,6 +477,22 @@ def _axis_tables_off_by_one(length, dim, base):
     return cos[1:].copy(), sin[1:].copy()
 
 
+def _rope3d_offsets_ignored(x, dtype, split, base=10000.0, tables=None, offsets=(0, 0, 0), grid=None):
+    B, T, H, W = x.shape[:4]
+    g = grid if grid is not None else (T + offsets[0], H + offsets[1], W + offsets[2])
+    if tables is None:
+        tables = orc.grid_tables(*g, split, base)
+    return orc.__dict__["_orig_rope3d"](x, dtype, split, base, tables, (0, 0, 0), g)
+
+
+def _rope3d_offsets_rotated(x, dtype, split, base=10000.0, tables=None, offsets=(0, 0, 0), grid=None):
+    t0, h0, w0 = offsets
+    B, T, H, W = x.shape[:4]
+    g = grid if grid is not None else (T + t0, H + h0, W + w0)
+    return orc.__dict__["_orig_rope3d"](x, dtype, split, base, tables, (h0, w0, t0) if
+                                        (h0 + T <= g[0] and w0 + H <= g[1] and t0 + W <= g[2]) else (0, 0, 0), g)
+
+
 MUTATIONS = [
     ("rotate_pairs", _rot_sign_flip),
     ("rotate_pairs", _rot_swap_cs),
@@ -447,6 +505,8 @@ MUTATIONS = [
     ("apply_rope_tokens", _apply_axis_order_swapped),
     ("apply_rope_tokens", _apply_rotate_half),
     ("axis_tables", _axis_tables_off_by_one),
+    ("rope3d", _rope3d_offsets_ignored),
+    ("rope3d", _rope3d_offsets_rotated),
 ]
 
 
