@@ -191,6 +191,45 @@ int ltx3drope_apply_qk(void* q_out, void* k_out, const void* q, const void* k, i
                        int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
                        ltx3drope_tables_t tables, void* stream);
 
+/*
+ * Shards.  A sequence- or tile-parallel rank holds a slab of a larger token
+ * grid; its tokens must take the table rows of their global coordinates.
+ * (Positions on the page are tile-local because the table cache key carries
+ * no offset: "Implementation breakdown", step 1.  The descriptor below is the
+ * offset that splitting one grid over several devices needs.)
+ *
+ * t_offset, h_offset, w_offset: global frame / row / column of the tensor's
+ * first frame / row / column.  The tables passed with a shard describe the
+ * whole grid: for each axis offset + local size <= the tables' size, else
+ * REASON_TABLE_GRID.  A token at local (t, h, w) is rotated with table rows
+ * (t + t_offset, h + h_offset, w + w_offset).
+ * inplace: 1 allows q_out == q and k_out == k exactly (partial overlaps stay
+ * refused).  In-place calls cannot be checked by the bit-exact gate (the
+ * inputs are overwritten); they use the fast kernel only once the
+ * configuration is TRUSTED (or the gate is off, or the fast path is forced),
+ * and the plain kernel otherwise.  A NULL descriptor means zero offsets,
+ * out of place.
+ */
+typedef struct {
+    int64_t t_offset, h_offset, w_offset;
+    int32_t inplace;
+    int32_t reserved;  /* must be 0 */
+} ltx3drope_shard_t;
+
+/* The precheck of a shard call: as ltx3drope_can_use, with the grid rule replaced by the shard's
+   containment rule and the in-place exception to the overlap rule.  Negative offsets or a non-zero
+   reserved field fail with REASON_TABLE_GRID. */
+int ltx3drope_can_use_shard(const void* q_out, const void* k_out, const void* q, const void* k, int dtype,
+                            int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
+                            const ltx3drope_shard_t* shard, ltx3drope_tables_t tables, int* reason);
+
+/* ltx3drope_apply_qk on a shard of the tables' grid (see above); B, T, H, W are the tensor's local
+   sizes.  Same statuses as ltx3drope_apply_qk; the gate key is the same as for an unsharded call of
+   the same local shape (offsets do not change which code runs). */
+int ltx3drope_apply_qk_shard(void* q_out, void* k_out, const void* q, const void* k, int dtype,
+                             int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
+                             const ltx3drope_shard_t* shard, ltx3drope_tables_t tables, void* stream);
+
 /* Gate state of one configuration key (LTX3DROPE_GATE_*), or a negative status. */
 int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W,
                          int64_t heads, int64_t head_dim, int64_t dim_t, int64_t dim_h, int64_t dim_w);

@@ -173,8 +173,19 @@ def _marshal(q, k, q_out, k_out):
             raise Ltx3dRopeUnsupported("OUTPUT_MISMATCH")
 
 
-def can_use(q, k, tabs: Tables, q_out=None, k_out=None) -> Tuple[bool, str]:
-    """The precheck: (True, "OK") if apply_qk would launch, else (False, reason)."""
+def _shard(offsets, inplace):
+    """A shard descriptor, or None for the unsharded, out-of-place entry points."""
+    if offsets is None and not inplace:
+        return None
+    t0, h0, w0 = (int(x) for x in (offsets or (0, 0, 0)))
+    return _lib.Shard(t0, h0, w0, 1 if inplace else 0, 0)
+
+
+def can_use(q, k, tabs: Tables, q_out=None, k_out=None, offsets=None, inplace: bool = False) -> Tuple[bool, str]:
+    """The precheck: (True, "OK") if apply_qk would launch, else (False, reason).
+
+    offsets: (t, h, w) position of q's first frame/row/column in the tables' grid (a shard);
+    inplace: allow q_out is q and k_out is k."""
     try:
         B, T, H, W, heads, D = _shape6(q)
         _marshal(q, k, q_out, k_out)
@@ -185,37 +196,60 @@ def can_use(q, k, tabs: Tables, q_out=None, k_out=None) -> Tuple[bool, str]:
     if (qo is None) != (ko is None):
         raise ValueError("give both q_out and k_out, or neither")
     reason = ctypes.c_int(0)
-    ok = _lib.lib().ltx3drope_can_use(qo, ko, q.data_ptr(), k.data_ptr(), _dtype_code(q), B, T, H, W, heads, D,
-                                      tabs.handle, ctypes.byref(reason))
+    sh = _shard(offsets, inplace)
+    if sh is None:
+        ok = _lib.lib().ltx3drope_can_use(qo, ko, q.data_ptr(), k.data_ptr(), _dtype_code(q), B, T, H, W, heads, D,
+                                          tabs.handle, ctypes.byref(reason))
+    else:
+        ok = _lib.lib().ltx3drope_can_use_shard(qo, ko, q.data_ptr(), k.data_ptr(), _dtype_code(q), B, T, H, W, heads,
+                                                D, ctypes.byref(sh), tabs.handle, ctypes.byref(reason))
     return bool(ok), _lib.REASONS.get(reason.value, str(reason.value))
 
 
-def apply_qk(q, k, tabs: Tables, q_out=None, k_out=None, stream=None):
-    """Rotate Q and K into fresh (or the given) output tensors with one kernel launch."""
+def apply_qk(q, k, tabs: Tables, q_out=None, k_out=None, stream=None, offsets=None, inplace: bool = False):
+    """Rotate Q and K into fresh (or the given) output tensors with one kernel launch.
+
+    offsets: (t, h, w) position of q's first frame/row/column in the tables' grid, for a shard of a
+    larger grid; inplace=True rotates q and k in place (q_out/k_out must then be None or q/k)."""
     torch = _torch()
     B, T, H, W, heads, D = _shape6(q)
     _marshal(q, k, q_out, k_out)
+    if inplace:
+        if (q_out is not None and q_out is not q) or (k_out is not None and k_out is not k):
+            raise ValueError("inplace=True writes into q and k")
+        q_out, k_out = q, k
     if q_out is None:
         q_out = torch.empty_like(q)
     if k_out is None:
         k_out = torch.empty_like(k)
-    st = _lib.lib().ltx3drope_apply_qk(q_out.data_ptr(), k_out.data_ptr(), q.data_ptr(), k.data_ptr(),
-                                       _dtype_code(q), B, T, H, W, heads, D, tabs.handle,
-                                       _stream_ptr(q.device, stream))
+    sh = _shard(offsets, inplace)
+    args = (q_out.data_ptr(), k_out.data_ptr(), q.data_ptr(), k.data_ptr(), _dtype_code(q), B, T, H, W, heads, D)
+    if sh is None:
+        st = _lib.lib().ltx3drope_apply_qk(*args, tabs.handle, _stream_ptr(q.device, stream))
+    else:
+        st = _lib.lib().ltx3drope_apply_qk_shard(*args, ctypes.byref(sh), tabs.handle, _stream_ptr(q.device, stream))
     if st in (_lib.E_UNSUPPORTED, _lib.E_TABLE_MISMATCH):
         reason = ctypes.c_int(0)
-        _lib.lib().ltx3drope_can_use(q_out.data_ptr(), k_out.data_ptr(), q.data_ptr(), k.data_ptr(),
-                                     _dtype_code(q), B, T, H, W, heads, D, tabs.handle, ctypes.byref(reason))
+        if sh is None:
+            _lib.lib().ltx3drope_can_use(*args, tabs.handle, ctypes.byref(reason))
+        else:
+            _lib.lib().ltx3drope_can_use_shard(*args, ctypes.byref(sh), tabs.handle, ctypes.byref(reason))
         raise Ltx3dRopeUnsupported(_lib.REASONS.get(reason.value, str(reason.value)), st)
     _check(st, "apply_qk")
     return q_out, k_out
 
 
-def forward_pair(q, k, split: Sequence[int], base: float = 10000.0, q_out=None, k_out=None, stream=None):
-    """Decoder-side entry: cached tables for q's (T, H, W) grid, then the fused rotation."""
+def forward_pair(q, k, split: Sequence[int], base: float = 10000.0, q_out=None, k_out=None, stream=None,
+                 grid: Optional[Sequence[int]] = None, offsets=None, inplace: bool = False):
+    """Decoder-side entry: cached tables for the grid, then the fused rotation.
+
+    grid defaults to q's own (T, H, W) (plus offsets, for a shard at the end of its grid)."""
     B, T, H, W, heads, D = _shape6(q)
-    with tables_build(T, H, W, split, base, device=q.device.index or 0, stream=stream) as tabs:
-        return apply_qk(q, k, tabs, q_out, k_out, stream)
+    if grid is None:
+        t0, h0, w0 = offsets or (0, 0, 0)
+        grid = (T + t0, H + h0, W + w0)
+    with tables_build(*grid, split, base, device=q.device.index or 0, stream=stream) as tabs:
+        return apply_qk(q, k, tabs, q_out, k_out, stream, offsets, inplace)
 
 
 def kernel_choice(q, k, tabs: Tables, q_out=None, k_out=None) -> str:

@@ -39,7 +39,8 @@ GATE_STATES = {0: "UNSEEN", 1: "TRUSTED", 2: "DISABLED"}
 # every symbol the header declares (checked by the CPU test suite)
 EXPORTS = (
     "ltx3drope_tables_build", "ltx3drope_tables_release", "ltx3drope_tables_describe", "ltx3drope_tables_read",
-    "ltx3drope_cache_clear", "ltx3drope_can_use", "ltx3drope_apply_qk", "ltx3drope_gate_state",
+    "ltx3drope_cache_clear", "ltx3drope_can_use", "ltx3drope_apply_qk", "ltx3drope_can_use_shard",
+    "ltx3drope_apply_qk_shard", "ltx3drope_gate_state",
     "ltx3drope_gate_reset", "ltx3drope_set_option", "ltx3drope_get_option", "ltx3drope_stats",
     "ltx3drope_stats_reset", "ltx3drope_kernel_choice", "ltx3drope_copy", "ltx3drope_status_string",
     "ltx3drope_reason_string", "ltx3drope_version",
@@ -53,6 +54,11 @@ fp = ctypes.POINTER(ctypes.c_float)
 class TablesDesc(ctypes.Structure):
     _fields_ = [("device", ctypes.c_int), ("T", i64), ("H", i64), ("W", i64), ("dim_t", i64), ("dim_h", i64),
                 ("dim_w", i64), ("base", ctypes.c_double), ("packed", vp), ("packed_pairs", i64)]
+
+
+class Shard(ctypes.Structure):
+    _fields_ = [("t_offset", i64), ("h_offset", i64), ("w_offset", i64), ("inplace", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -90,6 +96,10 @@ def lib() -> ctypes.CDLL:
             "ltx3drope_can_use": (ctypes.c_int, [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64, vp,
                                                  ctypes.POINTER(ctypes.c_int)]),
             "ltx3drope_apply_qk": (ctypes.c_int, [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64, vp, vp]),
+            "ltx3drope_can_use_shard": (ctypes.c_int, [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64,
+                                                       ctypes.POINTER(Shard), vp, ctypes.POINTER(ctypes.c_int)]),
+            "ltx3drope_apply_qk_shard": (ctypes.c_int, [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64,
+                                                        ctypes.POINTER(Shard), vp, vp]),
             "ltx3drope_gate_state": (ctypes.c_int, [ctypes.c_int, ctypes.c_int] + [i64] * 9),
             "ltx3drope_gate_reset": (ctypes.c_int, []),
             "ltx3drope_set_option": (ctypes.c_int, [ctypes.c_int, i64]),

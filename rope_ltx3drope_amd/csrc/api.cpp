@@ -141,18 +141,46 @@ int check_device_ptr(const void* p, size_t bytes, int device) {
     return LTX3DROPE_REASON_OK;
 }
 
+// Where the tensor sits in the tables' grid.  exact_grid: the unsharded rule of
+// the page's predicate (the tables' grid equals the tensor's); otherwise the
+// tensor may be any slab [offset, offset + size) of the tables' grid.
+struct Placement {
+    int64_t t0 = 0, h0 = 0, w0 = 0;
+    bool inplace = false;
+    bool exact_grid = true;
+};
+
+// Reads a shard descriptor; false if it is malformed.
+bool placement_from(const ltx3drope_shard_t* shard, Placement* out) {
+    *out = Placement();
+    out->exact_grid = false;
+    if (shard == nullptr) return true;
+    if (shard->reserved != 0 || (shard->inplace != 0 && shard->inplace != 1)) return false;
+    if (shard->t_offset < 0 || shard->h_offset < 0 || shard->w_offset < 0) return false;
+    out->t0 = shard->t_offset;
+    out->h0 = shard->h_offset;
+    out->w0 = shard->w_offset;
+    out->inplace = shard->inplace == 1;
+    return true;
+}
+
 // The precheck.  With check_outputs false, q_out and k_out are ignored (the caller
 // will allocate fresh outputs, which cannot overlap anything).
 int precheck(const void* q_out, const void* k_out, const void* q, const void* k, int dtype, int64_t B, int64_t T,
              int64_t H, int64_t W, int64_t heads, int64_t D, const ltx3drope_tables* tab, bool check_memory,
-             bool check_outputs = true) {
+             bool check_outputs, const Placement& pl) {
     if ((check_outputs && (!q_out || !k_out)) || !q || !k || !tab) return LTX3DROPE_REASON_NULLPTR;
     if (dtype != LTX3DROPE_DTYPE_F32 && dtype != LTX3DROPE_DTYPE_BF16) return LTX3DROPE_REASON_DTYPE;
     if (B <= 0 || T <= 0 || H <= 0 || W <= 0 || heads <= 0 || D <= 0) return LTX3DROPE_REASON_NONPOSITIVE_DIM;
     if (tab->dim_t <= 0 || tab->dim_h <= 0 || tab->dim_w <= 0 || tab->dim_t % 2 || tab->dim_h % 2 || tab->dim_w % 2)
         return LTX3DROPE_REASON_SPLIT_ODD;
     if (D != tab->dim_t + tab->dim_h + tab->dim_w) return LTX3DROPE_REASON_SPLIT_SUM;
-    if (tab->T != T || tab->H != H || tab->W != W) return LTX3DROPE_REASON_TABLE_GRID;
+    if (pl.exact_grid) {
+        if (tab->T != T || tab->H != H || tab->W != W) return LTX3DROPE_REASON_TABLE_GRID;
+    } else {
+        if (pl.t0 < 0 || pl.h0 < 0 || pl.w0 < 0 || pl.t0 > tab->T - T || pl.h0 > tab->H - H || pl.w0 > tab->W - W)
+            return LTX3DROPE_REASON_TABLE_GRID;
+    }
     const size_t es = dtype == LTX3DROPE_DTYPE_F32 ? 4 : 2;
     const uintptr_t pair = 2 * es;
     const void* ptrs[4] = {q, k, q_out, k_out};
@@ -168,11 +196,15 @@ int precheck(const void* q_out, const void* k_out, const void* q, const void* k,
     }
     if (numel >= lim) return LTX3DROPE_REASON_TOO_LARGE;
     const size_t bytes = static_cast<size_t>(numel) * es;
-    if (check_outputs &&
-        (ranges_overlap(q_out, bytes, q, bytes) || ranges_overlap(q_out, bytes, k, bytes) ||
-         ranges_overlap(k_out, bytes, q, bytes) || ranges_overlap(k_out, bytes, k, bytes) ||
-         ranges_overlap(q_out, bytes, k_out, bytes)))
-        return LTX3DROPE_REASON_OVERLAP;
+    if (check_outputs) {
+        // every output/input and output/output overlap is refused, except exact in-place aliasing
+        const bool q_inplace = pl.inplace && q_out == q;
+        const bool k_inplace = pl.inplace && k_out == k;
+        if ((!q_inplace && ranges_overlap(q_out, bytes, q, bytes)) || ranges_overlap(q_out, bytes, k, bytes) ||
+            ranges_overlap(k_out, bytes, q, bytes) || (!k_inplace && ranges_overlap(k_out, bytes, k, bytes)) ||
+            ranges_overlap(q_out, bytes, k_out, bytes))
+            return LTX3DROPE_REASON_OVERLAP;
+    }
     if (check_memory && !tab->host) {
         for (int i = 0; i < nptr; ++i) {
             const int r = check_device_ptr(ptrs[i], bytes, tab->device);
@@ -183,7 +215,8 @@ int precheck(const void* q_out, const void* k_out, const void* q, const void* k,
 }
 
 Problem make_problem(void* q_out, void* k_out, const void* q, const void* k, int dtype, int64_t B, int64_t T,
-                     int64_t H, int64_t W, int64_t heads, int64_t D, const ltx3drope_tables* tab) {
+                     int64_t H, int64_t W, int64_t heads, int64_t D, const ltx3drope_tables* tab,
+                     const Placement& pl) {
     Problem p;
     p.q_out = q_out;
     p.k_out = k_out;
@@ -201,6 +234,11 @@ Problem make_problem(void* q_out, void* k_out, const void* q, const void* k, int
     p.PH = static_cast<uint32_t>(tab->dim_h / 2);
     p.PW = static_cast<uint32_t>(tab->dim_w / 2);
     p.tab_pairs = static_cast<uint32_t>(tab->pairs);
+    p.tabT = static_cast<uint32_t>(tab->T);
+    p.tabH = static_cast<uint32_t>(tab->H);
+    p.t_off = static_cast<uint32_t>(pl.t0);
+    p.h_off = static_cast<uint32_t>(pl.h0);
+    p.w_off = static_cast<uint32_t>(pl.w0);
     return p;
 }
 
@@ -271,6 +309,64 @@ int64_t option(int which) {
 
 }  // namespace ltx3drope
 
+namespace ltx3drope {
+namespace {
+
+int apply_impl(void* q_out, void* k_out, const void* q, const void* k, int dtype, int64_t B, int64_t T, int64_t H,
+               int64_t W, int64_t heads, int64_t head_dim, ltx3drope_tables_t tables, void* stream_ptr,
+               const Placement& pl) {
+    if (tables != nullptr && tables->host) {
+        stats().rejected.fetch_add(1);
+        return LTX3DROPE_E_UNSUPPORTED;
+    }
+    const int r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, true, true, pl);
+    if (r != LTX3DROPE_REASON_OK) {
+        stats().rejected.fetch_add(1);
+        return status_for_reason(r);
+    }
+    const Problem p = make_problem(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, pl);
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    const int device = tables->device;
+    DeviceGuard guard(device);
+
+    const int64_t path = opts().path.load();
+    if (path == 2 || !fast_supported(p)) return run_kernel(Kernel::Plain, p, stream, device);
+    if (path == 1) return run_kernel(Kernel::Fast, p, stream, device);
+
+    const int64_t gate_mode = opts().gate.load();
+    if (gate_mode == 0) return run_kernel(Kernel::Fast, p, stream, device);
+    const GateKey key{device, dtype, B, T, H, W, heads, head_dim, tables->dim_t, tables->dim_h, tables->dim_w};
+    const int state = gate_get(key);
+    if (state == LTX3DROPE_GATE_DISABLED) return run_kernel(Kernel::Plain, p, stream, device);
+    const bool inplace = q_out == q || k_out == k;
+    if (inplace) {
+        // the inputs are overwritten, so this call cannot be verified: trust only an earlier verdict
+        return run_kernel(state == LTX3DROPE_GATE_TRUSTED && gate_mode == 1 ? Kernel::Fast : Kernel::Plain, p, stream,
+                          device);
+    }
+    if (state == LTX3DROPE_GATE_TRUSTED && gate_mode == 1) return run_kernel(Kernel::Fast, p, stream, device);
+
+    bool equal = false;
+    const int st = verify_fast(p, stream, device, &equal);
+    if (st != LTX3DROPE_OK) return st;
+    if (equal) {
+        if (state != LTX3DROPE_GATE_TRUSTED) stats().trusted.fetch_add(1);
+        gate_set(key, LTX3DROPE_GATE_TRUSTED);
+        return LTX3DROPE_OK;
+    }
+    stats().disabled.fetch_add(1);
+    gate_set(key, LTX3DROPE_GATE_DISABLED);
+    std::fprintf(stderr,
+                 "[ltx3drope] fast kernel differs from the plain kernel for dtype=%d B=%lld T=%lld H=%lld W=%lld "
+                 "heads=%lld D=%lld; this configuration now uses the plain kernel\n",
+                 dtype, static_cast<long long>(B), static_cast<long long>(T), static_cast<long long>(H),
+                 static_cast<long long>(W), static_cast<long long>(heads), static_cast<long long>(head_dim));
+    return run_kernel(Kernel::Plain, p, stream, device);  // overwrite with the reference result
+}
+
+}  // namespace
+}  // namespace ltx3drope
+
 using namespace ltx3drope;
 
 extern "C" {
@@ -334,7 +430,20 @@ int ltx3drope_can_use(const void* q_out, const void* k_out, const void* q, const
                       int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim, ltx3drope_tables_t tables,
                       int* reason) {
     const bool outputs = q_out != nullptr || k_out != nullptr;
-    const int r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, true, outputs);
+    const int r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, true, outputs, Placement());
+    if (reason) *reason = r;
+    return r == LTX3DROPE_REASON_OK ? 1 : 0;
+}
+
+int ltx3drope_can_use_shard(const void* q_out, const void* k_out, const void* q, const void* k, int dtype, int64_t B,
+                            int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
+                            const ltx3drope_shard_t* shard, ltx3drope_tables_t tables, int* reason) {
+    Placement pl;
+    int r = LTX3DROPE_REASON_TABLE_GRID;
+    if (placement_from(shard, &pl)) {
+        const bool outputs = q_out != nullptr || k_out != nullptr;
+        r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, true, outputs, pl);
+    }
     if (reason) *reason = r;
     return r == LTX3DROPE_REASON_OK ? 1 : 0;
 }
@@ -342,57 +451,28 @@ int ltx3drope_can_use(const void* q_out, const void* k_out, const void* q, const
 int ltx3drope_kernel_choice(const void* q_out, const void* k_out, const void* q, const void* k, int dtype, int64_t B,
                             int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
                             ltx3drope_tables_t tables) {
-    const int r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, false);
+    const int r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, false, true, Placement());
     if (r != LTX3DROPE_REASON_OK) return status_for_reason(r);
     const Problem p = make_problem(const_cast<void*>(q_out), const_cast<void*>(k_out), q, k, dtype, B, T, H, W, heads,
-                                   head_dim, tables);
+                                   head_dim, tables, Placement());
     return fast_supported(p) ? static_cast<int>(Kernel::Fast) : static_cast<int>(Kernel::Plain);
 }
 
 int ltx3drope_apply_qk(void* q_out, void* k_out, const void* q, const void* k, int dtype, int64_t B, int64_t T,
                        int64_t H, int64_t W, int64_t heads, int64_t head_dim, ltx3drope_tables_t tables,
                        void* stream_ptr) {
-    if (tables != nullptr && tables->host) {
+    return apply_impl(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, stream_ptr, Placement());
+}
+
+int ltx3drope_apply_qk_shard(void* q_out, void* k_out, const void* q, const void* k, int dtype, int64_t B, int64_t T,
+                             int64_t H, int64_t W, int64_t heads, int64_t head_dim, const ltx3drope_shard_t* shard,
+                             ltx3drope_tables_t tables, void* stream_ptr) {
+    Placement pl;
+    if (!placement_from(shard, &pl)) {
         stats().rejected.fetch_add(1);
-        return LTX3DROPE_E_UNSUPPORTED;
+        return LTX3DROPE_E_TABLE_MISMATCH;
     }
-    const int r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, true);
-    if (r != LTX3DROPE_REASON_OK) {
-        stats().rejected.fetch_add(1);
-        return status_for_reason(r);
-    }
-    const Problem p = make_problem(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables);
-    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-    const int device = tables->device;
-    DeviceGuard guard(device);
-
-    const int64_t path = opts().path.load();
-    if (path == 2 || !fast_supported(p)) return run_kernel(Kernel::Plain, p, stream, device);
-    if (path == 1) return run_kernel(Kernel::Fast, p, stream, device);
-
-    const int64_t gate_mode = opts().gate.load();
-    if (gate_mode == 0) return run_kernel(Kernel::Fast, p, stream, device);
-    const GateKey key{device, dtype, B, T, H, W, heads, head_dim, tables->dim_t, tables->dim_h, tables->dim_w};
-    const int state = gate_get(key);
-    if (state == LTX3DROPE_GATE_DISABLED) return run_kernel(Kernel::Plain, p, stream, device);
-    if (state == LTX3DROPE_GATE_TRUSTED && gate_mode == 1) return run_kernel(Kernel::Fast, p, stream, device);
-
-    bool equal = false;
-    const int st = verify_fast(p, stream, device, &equal);
-    if (st != LTX3DROPE_OK) return st;
-    if (equal) {
-        if (state != LTX3DROPE_GATE_TRUSTED) stats().trusted.fetch_add(1);
-        gate_set(key, LTX3DROPE_GATE_TRUSTED);
-        return LTX3DROPE_OK;
-    }
-    stats().disabled.fetch_add(1);
-    gate_set(key, LTX3DROPE_GATE_DISABLED);
-    std::fprintf(stderr,
-                 "[ltx3drope] fast kernel differs from the plain kernel for dtype=%d B=%lld T=%lld H=%lld W=%lld "
-                 "heads=%lld D=%lld; this configuration now uses the plain kernel\n",
-                 dtype, static_cast<long long>(B), static_cast<long long>(T), static_cast<long long>(H),
-                 static_cast<long long>(W), static_cast<long long>(heads), static_cast<long long>(head_dim));
-    return run_kernel(Kernel::Plain, p, stream, device);  // overwrite with the reference result
+    return apply_impl(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, stream_ptr, pl);
 }
 
 int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads,

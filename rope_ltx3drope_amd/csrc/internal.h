@@ -37,13 +37,15 @@ struct Problem {
     uint32_t B, T, H, W, heads, D;
     uint32_t PT, PH, PW;  // pairs per head in the t, h and w chunks
     uint32_t tab_pairs;
+    uint32_t tabT, tabH;  // the tables' grid frames and rows (section offsets of the packed layout)
+    uint32_t t_off, h_off, w_off;  // global coordinate of the tensor's first frame / row / column
 };
 
 enum class Kernel { Fast = 1, Plain = 2 };
 
 // Host-side decision whether the vectorised kernel covers this problem
-// (16-B aligned pointers, 16-B head rows, chunk boundaries on vector
-// boundaries, at most 512 vectors of 16 B per token).
+// (16-B aligned pointers, head rows of whole 16-B vectors, chunk boundaries on
+// vector boundaries).
 bool fast_supported(const Problem& p);
 
 // Launchers (kernels.hip).  They only enqueue; the caller checks hipGetLastError.

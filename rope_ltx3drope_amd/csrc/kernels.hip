@@ -99,6 +99,7 @@ struct PlainArgs {
     uint32_t PT, PH;
     uint32_t offH, offW;  // first pair of the h and w table sections
     uint32_t PW;
+    uint32_t t_off, h_off, w_off;  // global coordinate of the tensor's first frame / row / column
 };
 
 template <bool BF16, bool VERIFY>
@@ -116,11 +117,11 @@ __global__ void __launch_bounds__(kPlainBlock) rope_plain(PlainArgs a) {
         const uint32_t w = rem - h * a.W;
         uint32_t idx;
         if (j < a.PT) {
-            idx = t * a.PT + j;
+            idx = (t + a.t_off) * a.PT + j;
         } else if (j < a.PT + a.PH) {
-            idx = a.offH + h * a.PH + (j - a.PT);
+            idx = a.offH + (h + a.h_off) * a.PH + (j - a.PT);
         } else {
-            idx = a.offW + w * a.PW + (j - a.PT - a.PH);
+            idx = a.offW + (w + a.w_off) * a.PW + (j - a.PT - a.PH);
         }
         const float2 cs = a.tab[idx];
         if constexpr (BF16) {
@@ -184,6 +185,7 @@ struct FastArgs {
     uint32_t PT, PH;   // pairs in the t and h chunks
     uint32_t rowT4, rowH4, rowW4;  // float4 per table row of each section
     uint32_t offH4, offW4;         // first float4 of the h and w sections
+    uint32_t t_off, h_off, w_off;  // global coordinate of the tensor's first frame / row / column
 };
 
 // PPV pairs per 16-B vector: 4 for bf16, 2 for fp32.  Every chunk width is a
@@ -226,10 +228,12 @@ __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
         u = g - tok * a.HV;
     }
     const uint32_t n = tok % a.N;
-    const uint32_t t = n / a.HW;
-    const uint32_t rem = n - t * a.HW;
-    const uint32_t h = rem / a.W;
-    const uint32_t w = rem - h * a.W;
+    const uint32_t tl = n / a.HW;  // local coordinates, then global ones
+    const uint32_t rem = n - tl * a.HW;
+    const uint32_t hl = rem / a.W;
+    const uint32_t t = tl + a.t_off;
+    const uint32_t h = hl + a.h_off;
+    const uint32_t w = rem - hl * a.W + a.w_off;
     const uint32_t j0 = (u % a.V) * PPV;  // first pair of this vector inside its head
     uint32_t idx;
     if (j0 < a.PT) {
@@ -316,8 +320,11 @@ PlainArgs plain_args(const Problem& p, unsigned* mismatches) {
     a.PT = p.PT;
     a.PH = p.PH;
     a.PW = p.PW;
-    a.offH = p.T * p.PT;
-    a.offW = p.T * p.PT + p.H * p.PH;
+    a.offH = p.tabT * p.PT;
+    a.offW = p.tabT * p.PT + p.tabH * p.PH;
+    a.t_off = p.t_off;
+    a.h_off = p.h_off;
+    a.w_off = p.w_off;
     return a;
 }
 
@@ -367,8 +374,11 @@ hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
     a.rowT4 = p.PT / 2;
     a.rowH4 = p.PH / 2;
     a.rowW4 = p.PW / 2;
-    a.offH4 = p.T * p.PT / 2;
-    a.offW4 = (p.T * p.PT + p.H * p.PH) / 2;
+    a.offH4 = p.tabT * p.PT / 2;
+    a.offW4 = (p.tabT * p.PT + p.tabH * p.PH) / 2;
+    a.t_off = p.t_off;
+    a.h_off = p.h_off;
+    a.w_off = p.w_off;
     const uint32_t per_tensor = (a.total + kFastBlock - 1) / kFastBlock;
     if (per_tensor == 0) return hipSuccess;
     const uint32_t blocks = 2 * per_tensor;  // first half Q, second half K

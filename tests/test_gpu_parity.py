@@ -422,3 +422,88 @@ def test_copy_helper():
     rla.copy_bytes(dst, src)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+# ---------------------------------------------------------------------------
+# shards of a larger grid and in-place mode
+# ---------------------------------------------------------------------------
+
+SHARDS = [
+    # full grid (T, H, W), local shape, offsets, split, dtype
+    ((9, 6, 7), (2, 3, 6, 7, 4, 32), (5, 0, 0), (8, 8, 16), oracle.BF16),
+    ((4, 10, 7), (1, 4, 3, 7, 3, 24), (0, 6, 0), (8, 8, 8), oracle.BF16),
+    ((4, 5, 12), (1, 4, 5, 5, 2, 48), (0, 0, 7), (16, 16, 16), oracle.F32),
+    ((6, 8, 9), (2, 2, 3, 4, 8, 64), (3, 2, 5), (16, 24, 24), oracle.BF16),
+    ((6, 8, 9), (1, 2, 3, 4, 3, 12), (1, 4, 2), (2, 6, 4), oracle.BF16),  # plain kernel only
+]
+
+
+@pytest.mark.parametrize("grid,shape,offsets,split,dtype", SHARDS, ids=[str(s[2]) + s[4] for s in SHARDS])
+@pytest.mark.parametrize("path", [0, 2], ids=["auto", "plain"])
+def test_shards_full(grid, shape, offsets, split, dtype, path):
+    log(f"shard {shape} at {offsets} of {grid}, path {path}")
+    q, k = workloads.generate_custom(shape, dtype, seed=sum(offsets) + 100)
+    want_q, want_k = oracle.rope3d_qk(q, k, dtype, split, offsets=offsets, grid=grid)
+    rla.set_option(rla.OPT_PATH, path)
+    with rla.tables_build(*grid, split) as tab:
+        qo, ko = rla.apply_qk(to_dev(q, dtype), to_dev(k, dtype), tab, offsets=offsets)
+    torch.cuda.synchronize()
+    assert_bitexact(to_host(qo, dtype), want_q, dtype, "q")
+    assert_bitexact(to_host(ko, dtype), want_k, dtype, "k")
+
+
+def test_frame_shards_of_workload4_match_the_full_result():
+    """Sequence parallelism over frames at full size: workload 4 split into 8 frame shards
+    (2 frames each, t_offset = 2r) with the whole grid's tables; every shard's output equals
+    the same slab of the unsharded output, which is itself checked against the oracle."""
+    w = workloads.WORKLOADS[4]
+    log("workload 4 frame shards: generating inputs")
+    (q, k), = workloads.generate(w)
+    dq, dk = to_dev(q, w.dtype), to_dev(k, w.dtype)
+    with rla.tables_build(*w.grids[0], w.split, w.base) as tab:
+        fq, fk = rla.apply_qk(dq, dk, tab)
+        T = w.grids[0][0]
+        per = T // 8
+        for r in range(8):
+            sl = slice(r * per, (r + 1) * per)
+            sq, sk = dq[:, sl].contiguous(), dk[:, sl].contiguous()
+            oq, ok = rla.apply_qk(sq, sk, tab, offsets=(r * per, 0, 0))
+            assert torch.equal(oq.view(torch.int16), fq[:, sl].view(torch.int16)), r
+            assert torch.equal(ok.view(torch.int16), fk[:, sl].view(torch.int16)), r
+    torch.cuda.synchronize()
+    sampled_check(q, fq, w, 0, 1000, seed=45)
+    # a spatial tile as well: rows 32..63, columns 64..95 of every frame
+    with rla.tables_build(*w.grids[0], w.split, w.base) as tab:
+        tq = dq[:, :, 32:64, 64:96].contiguous()
+        tk = dk[:, :, 32:64, 64:96].contiguous()
+        oq, ok = rla.apply_qk(tq, tk, tab, offsets=(0, 32, 64))
+    torch.cuda.synchronize()
+    assert torch.equal(oq.view(torch.int16), fq[:, :, 32:64, 64:96].view(torch.int16))
+    assert torch.equal(ok.view(torch.int16), fk[:, :, 32:64, 64:96].view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.F32])
+def test_inplace_matches_out_of_place_and_respects_the_gate(dtype):
+    shape, split = (1, 3, 8, 8, 8, 64), (16, 24, 24)
+    q, k = workloads.generate_custom(shape, dtype, seed=31)
+    want_q, want_k = oracle.rope3d_qk(q, k, dtype, split)
+    with rla.tables_build(3, 8, 8, split) as tab:
+        # unseen configuration: an in-place call cannot be verified, so it runs the plain kernel
+        dq, dk = to_dev(q, dtype), to_dev(k, dtype)
+        rq, rk = rla.apply_qk(dq, dk, tab, inplace=True)
+        torch.cuda.synchronize()
+        assert rq.data_ptr() == dq.data_ptr() and rk.data_ptr() == dk.data_ptr()
+        s = rla.stats()
+        assert s["plain_launches"] == 1 and s["fast_launches"] == 0 and s["gate_verifications"] == 0
+        assert rla.gate_state(0, rla.DTYPE_BF16 if dtype == oracle.BF16 else rla.DTYPE_F32, shape, split) == "UNSEEN"
+        assert_bitexact(to_host(dq, dtype), want_q, dtype, "q in place (plain)")
+        assert_bitexact(to_host(dk, dtype), want_k, dtype, "k in place (plain)")
+        # an out-of-place call verifies and trusts the fast kernel; later in-place calls use it
+        rla.apply_qk(to_dev(q, dtype), to_dev(k, dtype), tab)
+        dq, dk = to_dev(q, dtype), to_dev(k, dtype)
+        rla.apply_qk(dq, dk, tab, inplace=True)
+        torch.cuda.synchronize()
+        s = rla.stats()
+        assert s["gate_verifications"] == 1 and s["fast_launches"] == 2
+        assert_bitexact(to_host(dq, dtype), want_q, dtype, "q in place (fast)")
+        assert_bitexact(to_host(dk, dtype), want_k, dtype, "k in place (fast)")

@@ -377,3 +377,55 @@ def test_copy_rejects_bad_arguments():
     assert L.ltx3drope_copy(None, None, 16, None) == _lib.E_INVALID
     assert L.ltx3drope_copy(1 << 32, (1 << 32) + 64, 15, None) == _lib.E_INVALID
     assert L.ltx3drope_copy(1 << 32, (1 << 32) + 8, 16, None) == _lib.E_INVALID
+
+
+# ---------------------------------------------------------------------------
+# shard placement and in-place aliasing (precheck only)
+# ---------------------------------------------------------------------------
+
+def call_can_use_shard(q_out, k_out, q, k, dtype, shape, shard, tab):
+    reason = ctypes.c_int(-1)
+    sh = None if shard is None else ctypes.byref(shard)
+    ok = L.ltx3drope_can_use_shard(q_out, k_out, q, k, dtype, *shape, sh, tab, ctypes.byref(reason))
+    return ok, _lib.REASONS[reason.value]
+
+
+def test_shard_containment_rules():
+    q, k, qo, ko = fake_ptrs(2)
+    bf = _lib.DTYPE_BF16
+    with rla.tables_build(8, 6, 5, SPLIT) as tab:
+        local = (1, 2, 6, 5, 2, 12)
+        assert call_can_use_shard(qo, ko, q, k, bf, local, _lib.Shard(6, 0, 0, 0, 0), tab.handle) == (1, "OK")
+        assert call_can_use_shard(qo, ko, q, k, bf, local, _lib.Shard(7, 0, 0, 0, 0), tab.handle) == (0, "TABLE_GRID")
+        assert call_can_use_shard(qo, ko, q, k, bf, local, _lib.Shard(-1, 0, 0, 0, 0), tab.handle) == (0, "TABLE_GRID")
+        assert call_can_use_shard(qo, ko, q, k, bf, local, _lib.Shard(0, 1, 0, 0, 0), tab.handle) == (0, "TABLE_GRID")
+        assert call_can_use_shard(qo, ko, q, k, bf, local, _lib.Shard(0, 0, 0, 0, 1), tab.handle) == (0, "TABLE_GRID")
+        assert call_can_use_shard(qo, ko, q, k, bf, local, _lib.Shard(0, 0, 0, 2, 0), tab.handle) == (0, "TABLE_GRID")
+        # spatial tiles: rows 2..4 and columns 1..3 of the 6x5 grid
+        tile = (1, 8, 3, 3, 2, 12)
+        assert call_can_use_shard(qo, ko, q, k, bf, tile, _lib.Shard(0, 2, 1, 0, 0), tab.handle) == (1, "OK")
+        assert call_can_use_shard(qo, ko, q, k, bf, tile, _lib.Shard(0, 4, 1, 0, 0), tab.handle) == (0, "TABLE_GRID")
+        assert call_can_use_shard(qo, ko, q, k, bf, tile, _lib.Shard(0, 2, 3, 0, 0), tab.handle) == (0, "TABLE_GRID")
+        # a NULL descriptor means offsets 0: a sub-grid at the origin is accepted by the shard entry ...
+        assert call_can_use_shard(qo, ko, q, k, bf, local, None, tab.handle) == (1, "OK")
+        # ... but the unsharded entry keeps the page's exact grid rule
+        assert call_can_use(qo, ko, q, k, bf, local, tab.handle) == (0, "TABLE_GRID")
+        full = (1, 8, 6, 5, 2, 12)
+        assert call_can_use(qo, ko, q, k, bf, full, tab.handle) == (1, "OK")
+
+
+def test_inplace_aliasing_rules():
+    q, k, qo, ko = fake_ptrs(2)
+    bf = _lib.DTYPE_BF16
+    with rla.tables_build(2, 3, 4, SPLIT) as tab:
+        inpl = _lib.Shard(0, 0, 0, 1, 0)
+        outp = _lib.Shard(0, 0, 0, 0, 0)
+        assert call_can_use_shard(q, k, q, k, bf, SHAPE, inpl, tab.handle) == (1, "OK")
+        assert call_can_use_shard(q, k, q, k, bf, SHAPE, outp, tab.handle) == (0, "OVERLAP")
+        assert call_can_use_shard(q + 4, k, q, k, bf, SHAPE, inpl, tab.handle) == (0, "OVERLAP")  # partial
+        assert call_can_use_shard(q, ko, q, k, bf, SHAPE, inpl, tab.handle) == (1, "OK")  # only Q in place
+        assert call_can_use_shard(k, q, q, k, bf, SHAPE, inpl, tab.handle) == (0, "OVERLAP")  # crossed
+        assert call_can_use_shard(q, q, q, q, bf, SHAPE, inpl, tab.handle) == (0, "OVERLAP")  # q aliases k
+        st = L.ltx3drope_apply_qk_shard(q, k, q, k, bf, *SHAPE, ctypes.byref(_lib.Shard(0, 0, 0, 3, 0)), tab.handle,
+                                         None)
+        assert st == _lib.E_TABLE_MISMATCH
