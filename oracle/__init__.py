@@ -12,7 +12,11 @@ unit-vector readback, identity at position 0, norm preservation, a +theta /
 brute-force per-element angle recomputation on tiny grids, the bf16 cast
 against torch's CPU cast and its closed-form properties.  Parity with
 sglang's own table bits is unpinned (no values are printed on the pages).
+
+oracle.neox: the rotate-half RoPE with a gathered cos/sin cache (pins in
+tests/test_neox_oracle_pins.py).
 """
+from . import neox  # noqa: F401
 from .rope import (  # noqa: F401
     BF16,
     F32,

@@ -156,3 +156,60 @@ def sample_tokens(num_tokens: int, count: int, seed: int) -> np.ndarray:
 
 def iter_calls(w: Workload) -> Iterator[int]:
     yield from w.calls
+
+
+# ---------------------------------------------------------------------------
+# rotate-half RoPE with a gathered cos/sin cache (text-encoder rotary)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class NeoxWorkload:
+    """q [tokens, q_heads, D], k [tokens, k_heads, D], positions [tokens], cache [max_position, D]."""
+
+    key: str
+    dtype: str
+    tokens: int
+    q_heads: int
+    k_heads: int
+    head_dim: int
+    max_position: int
+    cache_dtype: str
+    positions: str  # "arange" (a prefill) or "random"
+    seed: int
+
+    @property
+    def itemsize(self) -> int:
+        return 4 if self.dtype == F32 else 2
+
+    def algorithmic_bytes(self) -> int:
+        """Q and K read once and written once, the positions read once, one cache row read per token."""
+        qk = (self.q_heads + self.k_heads) * self.head_dim * self.itemsize
+        cache_row = self.head_dim * (4 if self.cache_dtype == F32 else 2)
+        return self.tokens * (2 * qk + 8 + cache_row)
+
+
+NEOX_WORKLOADS = {
+    "n1": NeoxWorkload("n1_f32_tiny", F32, 7, 4, 2, 16, 32, F32, "random", 10),
+    "n2": NeoxWorkload("n2_bf16_prefill_1k", BF16, 1024, 16, 8, 256, 4096, F32, "arange", 11),
+    "n3": NeoxWorkload("n3_bf16_random_pos", BF16, 3000, 8, 4, 128, 8192, BF16, "random", 12),
+    "n4": NeoxWorkload("n4_bf16_32k_tokens_h16_kv8_d256", BF16, 32768, 16, 8, 256, 32768, F32, "arange", 13),
+}
+
+
+def generate_neox(w: NeoxWorkload):
+    """(q, k, positions, cache).  The cache rows are cos|sin of angles drawn uniformly in
+    [-pi, pi) (float64 numpy cos/sin, rounded to the cache dtype by torch's cast): the op under
+    test only gathers and consumes them, so any unit-circle values are representative."""
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    n_q = w.tokens * w.q_heads * w.head_dim
+    n_k = w.tokens * w.k_heads * w.head_dim
+    q = _draw_normal(rng, n_q, w.dtype, None).reshape(w.tokens, w.q_heads, w.head_dim)
+    k = _draw_normal(rng, n_k, w.dtype, None).reshape(w.tokens, w.k_heads, w.head_dim)
+    if w.positions == "arange":
+        pos = np.arange(w.tokens, dtype=np.int64) % w.max_position
+    else:
+        pos = rng.integers(0, w.max_position, size=w.tokens, dtype=np.int64)
+    ang = rng.uniform(-np.pi, np.pi, size=(w.max_position, w.head_dim // 2))
+    rows = np.concatenate([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+    cache = rows if w.cache_dtype == F32 else _f32_to_bf16_bits_torch(rows.reshape(-1)).reshape(rows.shape)
+    return q, k, pos, cache
