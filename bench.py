@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--grid", type=int, default=0, help="grid index inside the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--op", choices=("rope3d", "neox"), default="rope3d",
+                    help="rope3d: the fused 3D RoPE (default); neox: the rotate-half RoPE with a gathered cache")
+    ap.add_argument("--neox-workload", default="n4")
     ap.add_argument("--rotate", type=int, default=0,
                     help="cycle through this many input/output sets (0: enough to exceed 2x the 256 MB "
                          "Infinity Cache, so every step streams from HBM)")
@@ -73,6 +76,8 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the fused RoPE needs no communication; see the sharding notes)", file=sys.stderr)
         sys.exit(2)
+    if args.op == "neox":
+        return main_neox(args)
 
     import numpy as np
     import torch
@@ -211,6 +216,79 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    if mism:
+        sys.exit(1)
+
+
+def main_neox(args):
+    """The rotate-half RoPE with a gathered cos/sin cache: one step = fresh outputs + one launch."""
+    import numpy as np
+    import torch
+
+    import oracle.neox as nx
+    import rope_ltx3drope_amd as rla
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.NEOX_WORKLOADS[args.neox_workload]
+    q_np, k_np, pos_np, cache_np = workloads.generate_neox(w)
+
+    def dev_t(x, dt):
+        if dt == workloads.BF16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    q, k = dev_t(q_np, w.dtype), dev_t(k_np, w.dtype)
+    pos, cache = torch.from_numpy(pos_np).to(dev), dev_t(cache_np, w.cache_dtype)
+    alg = w.algorithmic_bytes()
+    mall = 256 << 20
+    rotate = args.rotate or min(64, max(1, -(-4 * mall // alg)))
+    sets = [(q, k)] + [(q.clone(), k.clone()) for _ in range(rotate - 1)]
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        rla.neox_apply_qk(*sets[i % rotate], pos, cache)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    outs = []
+    t0 = time.perf_counter()
+    for i, (e0, e1) in enumerate(evs):
+        qi, ki = sets[(args.warmup + i) % rotate]
+        qo, ko = torch.empty_like(qi), torch.empty_like(ki)
+        e0.record(stream)
+        rla.neox_apply_qk(qi, ki, pos, cache, qo, ko)
+        e1.record(stream)
+        outs.append((qo, ko))
+        if len(outs) > rotate:
+            outs.pop(0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kavg = sum(a.elapsed_time(b) for a, b in evs) / len(evs) / 1e3
+    qo, ko = outs[-1]
+    ids = workloads.sample_tokens(w.tokens, 256, seed=99)
+    idx = torch.from_numpy(ids).to(dev)
+    mism = 0
+    for x_np, out in ((q_np, qo), (k_np, ko)):
+        want = nx.neox_rope(x_np[ids], w.dtype, pos_np[ids], cache_np, w.cache_dtype)
+        got = out[idx].cpu()
+        got = got.view(torch.int16).numpy().view(np.uint16) if w.dtype == workloads.BF16 else got.numpy()
+        mism += int((got.view(want.dtype) != want).sum())
+    st = rla.stats()
+    line = {
+        "metric": "rotate-half RoPE with gathered cos/sin cache, achieved HBM GB/s, bit-exact vs oracle",
+        "value": round(alg / (wall / args.steps) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded)",
+        "config": {"workload": w.key, "tokens": w.tokens, "q_heads": w.q_heads, "k_heads": w.k_heads,
+                   "head_dim": w.head_dim, "max_position": w.max_position, "cache_dtype": w.cache_dtype,
+                   "positions": w.positions, "algorithmic_bytes_per_step": alg, "input_sets": rotate},
+        "kernel": "neox_fast" if st["fast_launches"] else "neox_plain",
+        "kernel_avg_us": round(kavg * 1e6, 2),
+        "parity": {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0},
+        "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
     if mism:

@@ -230,6 +230,41 @@ int ltx3drope_apply_qk_shard(void* q_out, void* k_out, const void* q, const void
                              int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
                              const ltx3drope_shard_t* shard, ltx3drope_tables_t tables, void* stream);
 
+/*
+ * Rotate-half ("NeoX") RoPE with a position-gathered cos/sin cache: the text
+ * encoder's rotary (sglang PR #24660 page, "Key source snippets", the Gemma3
+ * rotary application; "Implementation breakdown", step 2).
+ *
+ * q [tokens, q_heads, head_dim], k [tokens, k_heads, head_dim] (the head
+ * counts may differ), contiguous, dtype F32 or BF16; positions [tokens] int64
+ * device array; cache [max_position, head_dim] of cache_dtype (F32 or BF16)
+ * holding cos in columns [0, head_dim/2) and sin in [head_dim/2, head_dim).
+ * For i < head_dim/2 with (c, s) = the token's cache row at i, converted to
+ * q's dtype:
+ *     out[i]            = R( R(x[i] * c)            + R(-x[i + head_dim/2] * s) )
+ *     out[i + head_dim/2] = R( R(x[i + head_dim/2] * c) + R(x[i] * s) )
+ * where R rounds an fp32 result to q's dtype (bf16: nearest even).  The
+ * outputs may alias their own input exactly (q_out == q, k_out == k); every
+ * other overlap is refused.  A position outside [0, max_position) is never
+ * read: that token's outputs are set to NaN and counted (see
+ * ltx3drope_neox_position_errors).  One launch for Q and K, on `stream`.
+ * Reasons: NULLPTR, DTYPE (q or cache dtype), NONPOSITIVE_DIM, SPLIT_ODD
+ * (odd head_dim), ALIGN (element alignment; positions 8 B), OVERLAP,
+ * TOO_LARGE (a tensor of 2^31 elements or more), NOT_DEVICE_PTR,
+ * TABLE_DEVICE (pointers on different devices), EXTENT.
+ */
+int ltx3drope_neox_can_use(const void* q_out, const void* k_out, const void* q, const void* k, int dtype,
+                           int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim,
+                           const int64_t* positions, const void* cache, int cache_dtype, int64_t max_position,
+                           int* reason);
+int ltx3drope_neox_apply_qk(void* q_out, void* k_out, const void* q, const void* k, int dtype,
+                            int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim,
+                            const int64_t* positions, const void* cache, int cache_dtype, int64_t max_position,
+                            void* stream);
+/* Number of (token, tensor) pairs whose position was outside the cache since the last reset, on
+   `device`.  Synchronizes the device.  reset = 1 clears the count afterwards. */
+int ltx3drope_neox_position_errors(int device, int reset, int64_t* count);
+
 /* Gate state of one configuration key (LTX3DROPE_GATE_*), or a negative status. */
 int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W,
                          int64_t heads, int64_t head_dim, int64_t dim_t, int64_t dim_h, int64_t dim_w);

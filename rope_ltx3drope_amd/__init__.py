@@ -34,7 +34,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "Ltx3dRopeError", "Ltx3dRopeUnsupported", "Tables", "tables", "tables_build", "can_use", "apply_qk",
     "forward_pair", "kernel_choice", "stats", "stats_reset", "set_option", "get_option", "gate_state", "gate_reset",
-    "cache_clear", "copy_bytes", "version",
+    "cache_clear", "copy_bytes", "version", "neox_can_use", "neox_apply_qk", "neox_position_errors",
 ]
 
 
@@ -250,6 +250,74 @@ def forward_pair(q, k, split: Sequence[int], base: float = 10000.0, q_out=None, 
         grid = (T + t0, H + h0, W + w0)
     with tables_build(*grid, split, base, device=q.device.index or 0, stream=stream) as tabs:
         return apply_qk(q, k, tabs, q_out, k_out, stream, offsets, inplace)
+
+
+def _neox_marshal(q, k, positions, cache, q_out, k_out):
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise Ltx3dRopeUnsupported("SHAPE_MISMATCH")
+    if k.dtype != q.dtype or positions.dtype != torch.int64:
+        raise Ltx3dRopeUnsupported("DTYPE")
+    if positions.numel() != q.shape[0] or cache.dim() != 2 or cache.shape[1] != q.shape[2]:
+        raise Ltx3dRopeUnsupported("SHAPE_MISMATCH")
+    for t in (q, k, positions, cache):
+        if not t.is_cuda or t.device != q.device:
+            raise Ltx3dRopeUnsupported("NOT_DEVICE_PTR")
+    for t in (q, k, positions, cache, q_out, k_out):
+        if t is not None and not t.is_contiguous():
+            raise Ltx3dRopeUnsupported("NOT_CONTIGUOUS")
+    for t, ref in ((q_out, q), (k_out, k)):
+        if t is not None and (t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device):
+            raise Ltx3dRopeUnsupported("OUTPUT_MISMATCH")
+
+
+def _neox_args(q_out, k_out, q, k, positions, cache):
+    return (q_out.data_ptr() if q_out is not None else None, k_out.data_ptr() if k_out is not None else None,
+            q.data_ptr(), k.data_ptr(), _dtype_code(q), int(q.shape[0]), int(q.shape[1]), int(k.shape[1]),
+            int(q.shape[2]), positions.data_ptr(), cache.data_ptr(), _dtype_code(cache), int(cache.shape[0]))
+
+
+def neox_can_use(q, k, positions, cache, q_out=None, k_out=None) -> Tuple[bool, str]:
+    """Precheck of the rotate-half RoPE: q [tokens, q_heads, D], k [tokens, k_heads, D],
+    positions [tokens] int64, cache [max_position, D] (cos half, then sin half)."""
+    try:
+        _neox_marshal(q, k, positions, cache, q_out, k_out)
+    except Ltx3dRopeUnsupported as e:
+        return False, e.reason
+    torch = _torch()
+    qo = q_out if q_out is not None else torch.empty_like(q)
+    ko = k_out if k_out is not None else torch.empty_like(k)
+    reason = ctypes.c_int(0)
+    ok = _lib.lib().ltx3drope_neox_can_use(*_neox_args(qo, ko, q, k, positions, cache), ctypes.byref(reason))
+    return bool(ok), _lib.REASONS.get(reason.value, str(reason.value))
+
+
+def neox_apply_qk(q, k, positions, cache, q_out=None, k_out=None, inplace: bool = False, stream=None):
+    """Rotate-half RoPE of Q and K with the cache rows gathered at `positions`, one launch."""
+    torch = _torch()
+    _neox_marshal(q, k, positions, cache, q_out, k_out)
+    if inplace:
+        q_out, k_out = q, k
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if k_out is None:
+        k_out = torch.empty_like(k)
+    args = _neox_args(q_out, k_out, q, k, positions, cache)
+    st = _lib.lib().ltx3drope_neox_apply_qk(*args, _stream_ptr(q.device, stream))
+    if st == _lib.E_UNSUPPORTED:
+        reason = ctypes.c_int(0)
+        _lib.lib().ltx3drope_neox_can_use(*args, ctypes.byref(reason))
+        raise Ltx3dRopeUnsupported(_lib.REASONS.get(reason.value, str(reason.value)), st)
+    _check(st, "neox_apply_qk")
+    return q_out, k_out
+
+
+def neox_position_errors(device: int = 0, reset: bool = False) -> int:
+    """(token, tensor) pairs whose position was outside the cache since the last reset (synchronizes)."""
+    n = ctypes.c_int64(0)
+    _check(_lib.lib().ltx3drope_neox_position_errors(int(device), 1 if reset else 0, ctypes.byref(n)),
+           "neox_position_errors")
+    return int(n.value)
 
 
 def kernel_choice(q, k, tabs: Tables, q_out=None, k_out=None) -> str:

@@ -20,6 +20,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <utility>
 
 #include "internal.h"
 
@@ -91,7 +92,8 @@ void gate_set(const GateKey& key, int s) {
 // ---- per-device resources ---------------------------------------------------
 
 struct DeviceRes {
-    unsigned* counter = nullptr;  // mismatch counter of the gate's verification
+    unsigned* counter = nullptr;  // [0]: mismatches of the gate's verification, [1]: out-of-cache positions
+    int cu_count = 0;
 };
 
 std::mutex g_dev_mu;
@@ -106,7 +108,19 @@ int device_res(int device, DeviceRes** out) {
             (void)hipGetLastError();
             return LTX3DROPE_E_NOMEM;
         }
+        // both counters start at zero (cleared by a kernel, then waited for once)
+        if (launch_zero_u32(static_cast<unsigned*>(mem), nullptr) != hipSuccess ||
+            launch_zero_u32(static_cast<unsigned*>(mem) + 1, nullptr) != hipSuccess ||
+            hipStreamSynchronize(nullptr) != hipSuccess) {
+            (void)hipGetLastError();
+            (void)hipFree(mem);
+            return LTX3DROPE_E_HIP;
+        }
         r.counter = static_cast<unsigned*>(mem);
+        if (hipDeviceGetAttribute(&r.cu_count, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+            (void)hipGetLastError();
+            r.cu_count = 256;
+        }
     }
     *out = &r;
     return LTX3DROPE_OK;
@@ -364,6 +378,67 @@ int apply_impl(void* q_out, void* k_out, const void* q, const void* k, int dtype
     return run_kernel(Kernel::Plain, p, stream, device);  // overwrite with the reference result
 }
 
+// ---- rotate-half RoPE with a gathered cache -------------------------------
+
+int neox_precheck(const void* q_out, const void* k_out, const void* q, const void* k, int dtype, int64_t tokens,
+                  int64_t q_heads, int64_t k_heads, int64_t D, const int64_t* positions, const void* cache,
+                  int cache_dtype, int64_t max_position, bool check_memory, int* device_out) {
+    if (!q_out || !k_out || !q || !k || !positions || !cache) return LTX3DROPE_REASON_NULLPTR;
+    for (int d : {dtype, cache_dtype})
+        if (d != LTX3DROPE_DTYPE_F32 && d != LTX3DROPE_DTYPE_BF16) return LTX3DROPE_REASON_DTYPE;
+    if (tokens <= 0 || q_heads <= 0 || k_heads <= 0 || D <= 0 || max_position <= 0)
+        return LTX3DROPE_REASON_NONPOSITIVE_DIM;
+    if (D % 2) return LTX3DROPE_REASON_SPLIT_ODD;
+    const size_t es = dtype == LTX3DROPE_DTYPE_F32 ? 4 : 2;
+    const size_t cs = cache_dtype == LTX3DROPE_DTYPE_F32 ? 4 : 2;
+    for (const void* p : {q_out, k_out, q, k})
+        if (reinterpret_cast<uintptr_t>(p) % es) return LTX3DROPE_REASON_ALIGN;
+    if (reinterpret_cast<uintptr_t>(cache) % cs || reinterpret_cast<uintptr_t>(positions) % 8)
+        return LTX3DROPE_REASON_ALIGN;
+    const int64_t lim = int64_t(1) << 31;
+    auto product_ok = [&](std::initializer_list<int64_t> fs) {
+        int64_t n = 1;
+        for (int64_t f : fs) {
+            if (f >= lim || n > lim / f) return false;
+            n *= f;
+        }
+        return n < lim;
+    };
+    if (!product_ok({tokens, q_heads, D}) || !product_ok({tokens, k_heads, D}) || !product_ok({max_position, D}))
+        return LTX3DROPE_REASON_TOO_LARGE;
+    const size_t qb = static_cast<size_t>(tokens * q_heads * D) * es;
+    const size_t kb = static_cast<size_t>(tokens * k_heads * D) * es;
+    const size_t pb = static_cast<size_t>(tokens) * 8;
+    const size_t cb = static_cast<size_t>(max_position * D) * cs;
+    // outputs: exact aliasing with their own input is allowed; nothing else may overlap an output
+    if ((q_out != q && ranges_overlap(q_out, qb, q, qb)) || ranges_overlap(q_out, qb, k, kb) ||
+        ranges_overlap(k_out, kb, q, qb) || (k_out != k && ranges_overlap(k_out, kb, k, kb)) ||
+        ranges_overlap(q_out, qb, k_out, kb))
+        return LTX3DROPE_REASON_OVERLAP;
+    for (const void* o : {q_out, k_out}) {
+        const size_t ob = o == q_out ? qb : kb;
+        if (ranges_overlap(o, ob, positions, pb) || ranges_overlap(o, ob, cache, cb)) return LTX3DROPE_REASON_OVERLAP;
+    }
+    if (check_memory) {
+        hipPointerAttribute_t a;
+        std::memset(&a, 0, sizeof(a));
+        if (hipPointerGetAttributes(&a, q) != hipSuccess) {
+            (void)hipGetLastError();
+            return LTX3DROPE_REASON_NOT_DEVICE_PTR;
+        }
+        if (a.type != hipMemoryTypeDevice) return LTX3DROPE_REASON_NOT_DEVICE_PTR;
+        const int device = a.device;
+        const std::pair<const void*, size_t> spans[6] = {{q, qb}, {k, kb}, {q_out, qb}, {k_out, kb},
+                                                         {positions, pb}, {cache, cb}};
+        for (const auto& sp : spans) {
+            const int r = check_device_ptr(sp.first, sp.second, device);
+            if (r != LTX3DROPE_REASON_OK) return r;
+        }
+        if (device_out) *device_out = device;
+    }
+    return LTX3DROPE_REASON_OK;
+}
+
 }  // namespace
 }  // namespace ltx3drope
 
@@ -473,6 +548,75 @@ int ltx3drope_apply_qk_shard(void* q_out, void* k_out, const void* q, const void
         return LTX3DROPE_E_TABLE_MISMATCH;
     }
     return apply_impl(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, stream_ptr, pl);
+}
+
+int ltx3drope_neox_can_use(const void* q_out, const void* k_out, const void* q, const void* k, int dtype,
+                           int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim,
+                           const int64_t* positions, const void* cache, int cache_dtype, int64_t max_position,
+                           int* reason) {
+    const int r = neox_precheck(q_out, k_out, q, k, dtype, tokens, q_heads, k_heads, head_dim, positions, cache,
+                                cache_dtype, max_position, true, nullptr);
+    if (reason) *reason = r;
+    return r == LTX3DROPE_REASON_OK ? 1 : 0;
+}
+
+int ltx3drope_neox_apply_qk(void* q_out, void* k_out, const void* q, const void* k, int dtype, int64_t tokens,
+                            int64_t q_heads, int64_t k_heads, int64_t head_dim, const int64_t* positions,
+                            const void* cache, int cache_dtype, int64_t max_position, void* stream_ptr) {
+    int device = -1;
+    const int r = neox_precheck(q_out, k_out, q, k, dtype, tokens, q_heads, k_heads, head_dim, positions, cache,
+                                cache_dtype, max_position, true, &device);
+    if (r != LTX3DROPE_REASON_OK) {
+        stats().rejected.fetch_add(1);
+        return LTX3DROPE_E_UNSUPPORTED;
+    }
+    DeviceGuard guard(device);
+    DeviceRes* res = nullptr;
+    const int st = device_res(device, &res);
+    if (st != LTX3DROPE_OK) return st;
+    NeoxProblem p;
+    p.q_out = q_out;
+    p.k_out = k_out;
+    p.q = q;
+    p.k = k;
+    p.positions = positions;
+    p.cache = cache;
+    p.dtype = dtype;
+    p.cache_dtype = cache_dtype;
+    p.tokens = static_cast<uint32_t>(tokens);
+    p.q_heads = static_cast<uint32_t>(q_heads);
+    p.k_heads = static_cast<uint32_t>(k_heads);
+    p.D = static_cast<uint32_t>(head_dim);
+    p.max_position = static_cast<uint32_t>(max_position > 0xffffffffll ? 0xffffffffll : max_position);
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    const bool fast = opts().path.load() != 2 && neox_fast_supported(p);
+    const hipError_t e = fast ? launch_neox_fast(p, res->counter + 1, stream)
+                              : launch_neox_plain(p, res->counter + 1, stream, res->cu_count);
+    if (e != hipSuccess || hipGetLastError() != hipSuccess) return LTX3DROPE_E_HIP;
+    (fast ? stats().fast : stats().plain).fetch_add(1);
+    return LTX3DROPE_OK;
+}
+
+int ltx3drope_neox_position_errors(int device, int reset, int64_t* count) {
+    if (count == nullptr || device < 0) return LTX3DROPE_E_INVALID;
+    DeviceGuard guard(device);
+    DeviceRes* res = nullptr;
+    const int st = device_res(device, &res);
+    if (st != LTX3DROPE_OK) return st;
+    unsigned host = 0;
+    if (hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(&host, res->counter + 1, sizeof(unsigned), hipMemcpyDeviceToHost) != hipSuccess) {
+        (void)hipGetLastError();
+        return LTX3DROPE_E_HIP;
+    }
+    *count = host;
+    if (reset) {
+        if (launch_zero_u32(res->counter + 1, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+            (void)hipGetLastError();
+            return LTX3DROPE_E_HIP;
+        }
+    }
+    return LTX3DROPE_OK;
 }
 
 int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads,

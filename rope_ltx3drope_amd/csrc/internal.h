@@ -57,6 +57,21 @@ hipError_t launch_verify(const Problem& p, unsigned* mismatches, hipStream_t str
 hipError_t launch_zero_u32(unsigned* ptr, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream, int device);
 
+// The rotate-half RoPE with a gathered cos/sin cache (neox.hip).
+struct NeoxProblem {
+    void* q_out;
+    void* k_out;
+    const void* q;
+    const void* k;
+    const int64_t* positions;
+    const void* cache;  // [max_position][D]: cos half, then sin half
+    int dtype, cache_dtype;
+    uint32_t tokens, q_heads, k_heads, D, max_position;
+};
+bool neox_fast_supported(const NeoxProblem& p);
+hipError_t launch_neox_fast(const NeoxProblem& p, unsigned* errors, hipStream_t stream);
+hipError_t launch_neox_plain(const NeoxProblem& p, unsigned* errors, hipStream_t stream, int cu_count);
+
 // Tables and cache (tables.cpp).
 int tables_build(int device, int64_t T, int64_t H, int64_t W, int64_t dim_t, int64_t dim_h, int64_t dim_w,
                  double base, hipStream_t stream, ltx3drope_tables_t* out);

@@ -429,3 +429,39 @@ def test_inplace_aliasing_rules():
         st = L.ltx3drope_apply_qk_shard(q, k, q, k, bf, *SHAPE, ctypes.byref(_lib.Shard(0, 0, 0, 3, 0)), tab.handle,
                                          None)
         assert st == _lib.E_TABLE_MISMATCH
+
+
+# ---------------------------------------------------------------------------
+# rotate-half RoPE precheck (rules decided before any device-memory query)
+# ---------------------------------------------------------------------------
+
+def call_neox_can_use(q_out, k_out, q, k, dtype, tokens, qh, kh, D, pos, cache, cdt, maxp):
+    reason = ctypes.c_int(-1)
+    ok = L.ltx3drope_neox_can_use(q_out, k_out, q, k, dtype, tokens, qh, kh, D, pos, cache, cdt, maxp,
+                                  ctypes.byref(reason))
+    return ok, _lib.REASONS[reason.value]
+
+
+def test_neox_precheck_rules():
+    base = 1 << 32
+    gap = 1 << 24
+    q, k, qo, ko, pos, cache = (base + i * gap for i in range(6))
+    bf, f32 = _lib.DTYPE_BF16, _lib.DTYPE_F32
+    good = (qo, ko, q, k, bf, 16, 4, 2, 64, pos, cache, f32, 128)
+    assert call_neox_can_use(*good[:9], None, *good[10:]) == (0, "NULLPTR")
+    assert call_neox_can_use(*good[:4], 5, *good[5:]) == (0, "DTYPE")
+    assert call_neox_can_use(*good[:11], 9, good[12]) == (0, "DTYPE")
+    assert call_neox_can_use(*good[:5], 0, *good[6:]) == (0, "NONPOSITIVE_DIM")
+    assert call_neox_can_use(*good[:12], 0) == (0, "NONPOSITIVE_DIM")
+    assert call_neox_can_use(*good[:8], 63, *good[9:]) == (0, "SPLIT_ODD")
+    assert call_neox_can_use(qo + 1, *good[1:]) == (0, "ALIGN")
+    assert call_neox_can_use(*good[:9], pos + 4, *good[10:]) == (0, "ALIGN")
+    assert call_neox_can_use(*good[:10], cache + 2, *good[11:]) == (0, "ALIGN")
+    assert call_neox_can_use(*good[:5], 1 << 20, 1 << 10, 2, 64, *good[9:]) == (0, "TOO_LARGE")
+    assert call_neox_can_use(q + 64, *good[1:]) == (0, "OVERLAP")        # partial overlap of q_out and q
+    assert call_neox_can_use(qo, cache + 16, *good[2:]) == (0, "OVERLAP")  # k_out over the cache
+    assert call_neox_can_use(pos, *good[1:]) == (0, "OVERLAP")             # q_out over the positions
+    assert call_neox_can_use(k, *good[1:]) == (0, "OVERLAP")               # q_out over k
+    # exact in-place aliasing passes every host rule (device memory is checked last)
+    ok, reason = call_neox_can_use(q, k, *good[2:])
+    assert reason in ("NOT_DEVICE_PTR", "OK")

@@ -1,0 +1,162 @@
+"""GPU parity of the rotate-half RoPE (through the C ABI) against oracle.neox, 0 ULP."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.neox as nx
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+rla = pytest.importorskip("rope_ltx3drope_amd")
+from rope_ltx3drope_amd import _lib  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(f"[neox-gpu] {msg}", flush=True)
+
+
+@pytest.fixture(autouse=True)
+def fresh():
+    assert torch.cuda.is_available()
+    _lib.lib()
+    rla.set_option(rla.OPT_PATH, 0)
+    rla.stats_reset()
+    rla.neox_position_errors(0, reset=True)
+    yield
+    rla.set_option(rla.OPT_PATH, 0)
+    torch.cuda.synchronize()
+
+
+def to_dev(x, dtype):
+    if dtype == oracle.BF16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def to_host(t, dtype):
+    if dtype == oracle.BF16:
+        return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+    return t.detach().cpu().numpy()
+
+
+def assert_bitexact(got, want, dtype, what):
+    g = got.view(np.uint32 if dtype == oracle.F32 else np.uint16)
+    w = want.view(np.uint32 if dtype == oracle.F32 else np.uint16)
+    neq = g != w
+    if neq.any():
+        both_nan = np.isnan(oracle.to_f32(got, dtype)) & np.isnan(oracle.to_f32(want, dtype))
+        neq &= ~both_nan
+    n = int(neq.sum())
+    assert n == 0, f"{what}: {n} mismatching elements, first at {np.argwhere(neq)[:3].tolist()}"
+
+
+def run(w, path, q=None, k=None, pos=None, cache=None, inplace=False):
+    if q is None:
+        q, k, pos, cache = workloads.generate_neox(w)
+    rla.set_option(rla.OPT_PATH, path)
+    dq, dk = to_dev(q, w.dtype), to_dev(k, w.dtype)
+    dpos = torch.from_numpy(pos).to(DEV)
+    dcache = to_dev(cache, w.cache_dtype)
+    qo, ko = rla.neox_apply_qk(dq, dk, dpos, dcache, inplace=inplace)
+    torch.cuda.synchronize()
+    if inplace:
+        assert qo.data_ptr() == dq.data_ptr() and ko.data_ptr() == dk.data_ptr()
+    return (q, k, pos, cache), to_host(qo, w.dtype), to_host(ko, w.dtype)
+
+
+CASES = ["n1", "n2", "n3"]
+
+
+@pytest.mark.parametrize("key", CASES)
+@pytest.mark.parametrize("path", [0, 2], ids=["fast", "plain"])
+def test_workloads_full(key, path):
+    w = workloads.NEOX_WORKLOADS[key]
+    log(f"{w.key} path {path}")
+    (q, k, pos, cache), gq, gk = run(w, path)
+    assert_bitexact(gq, nx.neox_rope(q, w.dtype, pos, cache, w.cache_dtype), w.dtype, "q")
+    assert_bitexact(gk, nx.neox_rope(k, w.dtype, pos, cache, w.cache_dtype), w.dtype, "k")
+    s = rla.stats()
+    if path == 2:
+        assert s["plain_launches"] == 1 and s["fast_launches"] == 0
+    else:
+        assert s["fast_launches"] == 1
+
+
+SHAPES = [
+    # dtype, tokens, q_heads, k_heads, D, max_pos, cache dtype  (plain-only shapes included)
+    (oracle.BF16, 37, 5, 1, 32, 64, oracle.F32),
+    (oracle.BF16, 13, 2, 3, 48, 20, oracle.BF16),
+    (oracle.BF16, 9, 3, 2, 20, 30, oracle.F32),   # half row of 10 bf16: not whole 16-byte vectors
+    (oracle.F32, 21, 4, 4, 8, 40, oracle.F32),
+    (oracle.F32, 17, 2, 1, 16, 9, oracle.BF16),
+    (oracle.F32, 5, 1, 1, 2, 3, oracle.F32),
+    (oracle.BF16, 300, 16, 8, 256, 512, oracle.BF16),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+@pytest.mark.parametrize("inplace", [False, True], ids=["fresh", "inplace"])
+def test_shapes_full(shape, inplace):
+    dtype, tokens, qh, kh, D, maxp, cdt = shape
+    w = workloads.NeoxWorkload("s", dtype, tokens, qh, kh, D, maxp, cdt, "random", tokens + D)
+    (q, k, pos, cache), gq, gk = run(w, 0, inplace=inplace)
+    assert_bitexact(gq, nx.neox_rope(q, dtype, pos, cache, cdt), dtype, "q")
+    assert_bitexact(gk, nx.neox_rope(k, dtype, pos, cache, cdt), dtype, "k")
+
+
+def test_out_of_range_positions_are_flagged_not_read():
+    w = workloads.NEOX_WORKLOADS["n3"]
+    q, k, pos, cache = workloads.generate_neox(w)
+    bad = pos.copy()
+    bad[[3, 10, 11]] = [-1, w.max_position, 1 << 40]
+    for path in (0, 2):
+        rla.neox_position_errors(0, reset=True)
+        _, gq, gk = run(w, path, q, k, bad, cache)
+        assert rla.neox_position_errors(0, reset=True) == 6  # 3 tokens x (Q, K)
+        good = np.ones(len(pos), bool)
+        good[[3, 10, 11]] = False
+        want_q = nx.neox_rope(q[good], w.dtype, pos[good], cache, w.cache_dtype)
+        assert_bitexact(gq[good], want_q, w.dtype, "q on valid tokens")
+        assert np.isnan(oracle.to_f32(gq[~good], w.dtype)).all()
+        assert np.isnan(oracle.to_f32(gk[~good], w.dtype)).all()
+
+
+def test_full_size_sampled_and_fast_equals_plain():
+    w = workloads.NEOX_WORKLOADS["n4"]
+    log("n4: generating inputs")
+    q, k, pos, cache = workloads.generate_neox(w)
+    dq, dk = to_dev(q, w.dtype), to_dev(k, w.dtype)
+    dpos, dcache = torch.from_numpy(pos).to(DEV), to_dev(cache, w.cache_dtype)
+    fq, fk = rla.neox_apply_qk(dq, dk, dpos, dcache)
+    rla.set_option(rla.OPT_PATH, 2)
+    pq, pk = rla.neox_apply_qk(dq, dk, dpos, dcache)
+    torch.cuda.synchronize()
+    assert torch.equal(fq.view(torch.int16), pq.view(torch.int16))
+    assert torch.equal(fk.view(torch.int16), pk.view(torch.int16))
+    ids = workloads.sample_tokens(w.tokens, 1500, seed=77)
+    idx = torch.from_numpy(ids).to(DEV)
+    assert_bitexact(to_host(fq[idx], w.dtype), nx.neox_rope(q[ids], w.dtype, pos[ids], cache, w.cache_dtype),
+                    w.dtype, "q sampled")
+    assert_bitexact(to_host(fk[idx], w.dtype), nx.neox_rope(k[ids], w.dtype, pos[ids], cache, w.cache_dtype),
+                    w.dtype, "k sampled")
+
+
+def test_precheck_refusals_on_device():
+    w = workloads.NEOX_WORKLOADS["n1"]
+    q, k, pos, cache = workloads.generate_neox(w)
+    dq, dk = to_dev(q, w.dtype), to_dev(k, w.dtype)
+    dpos, dcache = torch.from_numpy(pos).to(DEV), to_dev(cache, w.cache_dtype)
+    assert rla.neox_can_use(dq, dk, dpos, dcache) == (True, "OK")
+    assert rla.neox_can_use(dq, dk, dpos.int(), dcache)[0] is False
+    assert rla.neox_can_use(dq, dk, dpos.cpu(), dcache) == (False, "NOT_DEVICE_PTR")
+    with pytest.raises(rla.Ltx3dRopeUnsupported):
+        rla.neox_apply_qk(dq, dk, dpos, dcache[:, :8])
+    with pytest.raises(rla.Ltx3dRopeUnsupported):
+        rla.neox_apply_qk(dq[:, :, :15].contiguous(), dk[:, :, :15].contiguous(), dpos, dcache[:, :15].contiguous())
+    assert rla.stats()["fast_launches"] == 0 and rla.stats()["plain_launches"] == 0
