@@ -61,8 +61,10 @@ def parse():
     ap.add_argument("--grid", type=int, default=0, help="grid index inside the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--op", choices=("rope3d", "neox"), default="rope3d",
-                    help="rope3d: the fused 3D RoPE (default); neox: the rotate-half RoPE with a gathered cache")
+    ap.add_argument("--op", choices=("rope3d", "neox", "patchify", "unpatchify"), default="rope3d",
+                    help="rope3d: the fused 3D RoPE (default); neox: the rotate-half RoPE with a gathered cache; "
+                         "patchify / unpatchify: the stage-5 space-to-depth and its inverse")
+    ap.add_argument("--patch-workload", default="p6")
     ap.add_argument("--neox-workload", default="n4")
     ap.add_argument("--rotate", type=int, default=0,
                     help="cycle through this many input/output sets (0: enough to exceed 2x the 256 MB "
@@ -78,6 +80,8 @@ def main():
         sys.exit(2)
     if args.op == "neox":
         return main_neox(args)
+    if args.op in ("patchify", "unpatchify"):
+        return main_patch(args)
 
     import numpy as np
     import torch
@@ -286,6 +290,67 @@ def main_neox(args):
         "kernel": "neox_fast" if st["fast_launches"] else "neox_plain",
         "kernel_avg_us": round(kavg * 1e6, 2),
         "parity": {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0},
+        "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    if mism:
+        sys.exit(1)
+
+
+def main_patch(args):
+    """Space-to-depth (or its inverse) of a 5-D tensor: one step = a fresh output + one launch."""
+    import numpy as np
+    import torch
+
+    import oracle.patchify as pf
+    import rope_ltx3drope_amd as rla
+    import workloads
+
+    dev = torch.device("cuda:0")
+    shape, p, eb = workloads.PATCH_WORKLOADS[args.patch_workload]
+    x_np = workloads.generate_patch(shape, eb, seed=6)
+    signed = {1: np.uint8, 2: np.int16, 4: np.int32, 8: np.int64}[eb]
+    x = torch.from_numpy(x_np.view(signed)).to(dev)
+    inverse = args.op == "unpatchify"
+    src = rla.patchify(x, p) if inverse else x
+    fn = (lambda t: rla.unpatchify(t, p)) if inverse else (lambda t: rla.patchify(t, p))
+    alg = 2 * x.numel() * eb
+    mall = 256 << 20
+    rotate = args.rotate or min(64, max(1, -(-4 * mall // alg)))
+    sets = [src] + [src.clone() for _ in range(rotate - 1)]
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        fn(sets[i % rotate])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    outs = []
+    t0 = time.perf_counter()
+    for i, (e0, e1) in enumerate(evs):
+        e0.record(stream)
+        outs.append(fn(sets[(args.warmup + i) % rotate]))
+        e1.record(stream)
+        if len(outs) > rotate:
+            outs.pop(0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kavg = sum(a.elapsed_time(b) for a, b in evs) / len(evs) / 1e3
+    got = outs[-1].cpu().numpy().view(x_np.dtype)
+    want = x_np if inverse else pf.patchify(x_np, p)
+    mism = int((got != want).sum())
+    st = rla.stats()
+    line = {
+        "metric": f"{args.op} (stage-5 space-to-depth) achieved HBM GB/s, bit-exact vs oracle",
+        "value": round(alg / (wall / args.steps) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": {1: "u8", 2: "bf16-bits", 4: "f32-bits", 8: "u64"}[eb],
+        "data": "synthetic (seeded random bit patterns)",
+        "config": {"workload": args.patch_workload, "shape": list(shape), "p": p, "elem_bytes": eb,
+                   "algorithmic_bytes_per_step": alg, "input_sets": rotate},
+        "kernel": "patch_fast" if st["fast_launches"] else "patch_plain",
+        "kernel_avg_us": round(kavg * 1e6, 2),
+        "parity": {"compared_elements": int(got.size), "mismatching_elements": mism, "tolerance_ulp": 0},
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": None,

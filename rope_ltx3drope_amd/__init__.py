@@ -34,7 +34,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "Ltx3dRopeError", "Ltx3dRopeUnsupported", "Tables", "tables", "tables_build", "can_use", "apply_qk",
     "forward_pair", "kernel_choice", "stats", "stats_reset", "set_option", "get_option", "gate_state", "gate_reset",
-    "cache_clear", "copy_bytes", "version", "neox_can_use", "neox_apply_qk", "neox_position_errors",
+    "cache_clear", "copy_bytes", "version", "neox_can_use", "neox_apply_qk", "neox_position_errors", "patchify",
+    "unpatchify",
 ]
 
 
@@ -318,6 +319,47 @@ def neox_position_errors(device: int = 0, reset: bool = False) -> int:
     _check(_lib.lib().ltx3drope_neox_position_errors(int(device), 1 if reset else 0, ctypes.byref(n)),
            "neox_position_errors")
     return int(n.value)
+
+
+def patchify(x, p: int, out=None, stream=None):
+    """Space-to-depth (B, C, F, H, W) -> (B, C*p*p, F, H/p, W/p), channels packed as
+    (channel, width offset, height offset)."""
+    torch = _torch()
+    if x.dim() != 5 or not x.is_cuda or not x.is_contiguous():
+        raise Ltx3dRopeUnsupported("SHAPE_MISMATCH")
+    B, C, F, H, W = (int(s) for s in x.shape)
+    if p < 1 or H % p or W % p:
+        raise ValueError("H and W must be multiples of p")
+    shape = (B, C * p * p, F, H // p, W // p)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+        raise Ltx3dRopeUnsupported("OUTPUT_MISMATCH")
+    st = _lib.lib().ltx3drope_patchify(out.data_ptr(), x.data_ptr(), x.element_size(), B, C, F, H, W, int(p),
+                                      _stream_ptr(x.device, stream))
+    if st == _lib.E_UNSUPPORTED:
+        raise Ltx3dRopeUnsupported("PRECHECK", st)
+    _check(st, "patchify")
+    return out
+
+
+def unpatchify(y, p: int, out=None, stream=None):
+    """Inverse of patchify: (B, C*p*p, F, H/p, W/p) -> (B, C, F, H, W)."""
+    torch = _torch()
+    if y.dim() != 5 or not y.is_cuda or not y.is_contiguous() or int(y.shape[1]) % (p * p):
+        raise Ltx3dRopeUnsupported("SHAPE_MISMATCH")
+    B, Cpp, F, Hp, Wp = (int(s) for s in y.shape)
+    C, H, W = Cpp // (p * p), Hp * p, Wp * p
+    if out is None:
+        out = torch.empty((B, C, F, H, W), dtype=y.dtype, device=y.device)
+    elif tuple(out.shape) != (B, C, F, H, W) or out.dtype != y.dtype or not out.is_contiguous() or out.device != y.device:
+        raise Ltx3dRopeUnsupported("OUTPUT_MISMATCH")
+    st = _lib.lib().ltx3drope_unpatchify(out.data_ptr(), y.data_ptr(), y.element_size(), B, C, F, H, W, int(p),
+                                        _stream_ptr(y.device, stream))
+    if st == _lib.E_UNSUPPORTED:
+        raise Ltx3dRopeUnsupported("PRECHECK", st)
+    _check(st, "unpatchify")
+    return out
 
 
 def kernel_choice(q, k, tabs: Tables, q_out=None, k_out=None) -> str:

@@ -619,6 +619,86 @@ int ltx3drope_neox_position_errors(int device, int reset, int64_t* count) {
     return LTX3DROPE_OK;
 }
 
+}  // extern "C"
+
+namespace ltx3drope {
+namespace {
+
+int patch_call(void* dst, const void* src, int elem_bytes, int64_t B, int64_t C, int64_t F, int64_t H, int64_t W,
+               int64_t p, void* stream_ptr, bool inverse) {
+    if (!dst || !src) return LTX3DROPE_E_INVALID;
+    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return LTX3DROPE_E_INVALID;
+    if (B <= 0 || C <= 0 || F <= 0 || H <= 0 || W <= 0 || p <= 0 || H % p || W % p) return LTX3DROPE_E_INVALID;
+    const int64_t lim = int64_t(1) << 31;
+    int64_t numel = 1;
+    for (int64_t f : {B, C, F, H, W}) {
+        if (f >= lim || numel > lim / f) {
+            stats().rejected.fetch_add(1);
+            return LTX3DROPE_E_UNSUPPORTED;
+        }
+        numel *= f;
+    }
+    if (numel >= lim || p * p > lim / C) {
+        stats().rejected.fetch_add(1);
+        return LTX3DROPE_E_UNSUPPORTED;
+    }
+    const size_t bytes = static_cast<size_t>(numel) * static_cast<size_t>(elem_bytes);
+    if (reinterpret_cast<uintptr_t>(dst) % elem_bytes || reinterpret_cast<uintptr_t>(src) % elem_bytes ||
+        ranges_overlap(dst, bytes, src, bytes)) {
+        stats().rejected.fetch_add(1);
+        return LTX3DROPE_E_UNSUPPORTED;
+    }
+    hipPointerAttribute_t a;
+    std::memset(&a, 0, sizeof(a));
+    if (hipPointerGetAttributes(&a, src) != hipSuccess || a.type != hipMemoryTypeDevice) {
+        (void)hipGetLastError();
+        stats().rejected.fetch_add(1);
+        return LTX3DROPE_E_UNSUPPORTED;
+    }
+    const int device = a.device;
+    if (check_device_ptr(src, bytes, device) != LTX3DROPE_REASON_OK ||
+        check_device_ptr(dst, bytes, device) != LTX3DROPE_REASON_OK) {
+        stats().rejected.fetch_add(1);
+        return LTX3DROPE_E_UNSUPPORTED;
+    }
+    DeviceGuard guard(device);
+    DeviceRes* res = nullptr;
+    const int st = device_res(device, &res);
+    if (st != LTX3DROPE_OK) return st;
+    PatchProblem pp;
+    pp.src = src;
+    pp.dst = dst;
+    pp.elem_bytes = static_cast<uint32_t>(elem_bytes);
+    pp.B = static_cast<uint32_t>(B);
+    pp.C = static_cast<uint32_t>(C);
+    pp.F = static_cast<uint32_t>(F);
+    pp.H = static_cast<uint32_t>(H);
+    pp.W = static_cast<uint32_t>(W);
+    pp.p = static_cast<uint32_t>(p);
+    pp.force_plain = opts().path.load() == 2;
+    const bool fast = !pp.force_plain && patch_fast_supported(pp);
+    if (launch_patch(pp, inverse, static_cast<hipStream_t>(stream_ptr), res->cu_count) != hipSuccess ||
+        hipGetLastError() != hipSuccess)
+        return LTX3DROPE_E_HIP;
+    (fast ? stats().fast : stats().plain).fetch_add(1);
+    return LTX3DROPE_OK;
+}
+
+}  // namespace
+}  // namespace ltx3drope
+
+extern "C" {
+
+int ltx3drope_patchify(void* y, const void* x, int elem_bytes, int64_t B, int64_t C, int64_t F, int64_t H, int64_t W,
+                       int64_t p, void* stream) {
+    return patch_call(y, x, elem_bytes, B, C, F, H, W, p, stream, false);
+}
+
+int ltx3drope_unpatchify(void* x, const void* y, int elem_bytes, int64_t B, int64_t C, int64_t F, int64_t H,
+                         int64_t W, int64_t p, void* stream) {
+    return patch_call(x, y, elem_bytes, B, C, F, H, W, p, stream, true);
+}
+
 int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads,
                          int64_t head_dim, int64_t dim_t, int64_t dim_h, int64_t dim_w) {
     return gate_get(GateKey{device, dtype, B, T, H, W, heads, head_dim, dim_t, dim_h, dim_w});

@@ -72,6 +72,17 @@ bool neox_fast_supported(const NeoxProblem& p);
 hipError_t launch_neox_fast(const NeoxProblem& p, unsigned* errors, hipStream_t stream);
 hipError_t launch_neox_plain(const NeoxProblem& p, unsigned* errors, hipStream_t stream, int cu_count);
 
+// Stage-5 space-to-depth and its inverse (patchify.hip).  Dimensions are those of
+// the unpatched tensor (B, C, F, H, W); src/dst are the input/output of the call.
+struct PatchProblem {
+    const void* src;
+    void* dst;
+    uint32_t elem_bytes, B, C, F, H, W, p;
+    bool force_plain;
+};
+bool patch_fast_supported(const PatchProblem& p);
+hipError_t launch_patch(const PatchProblem& p, bool inverse, hipStream_t stream, int cu_count);
+
 // Tables and cache (tables.cpp).
 int tables_build(int device, int64_t T, int64_t H, int64_t W, int64_t dim_t, int64_t dim_h, int64_t dim_w,
                  double base, hipStream_t stream, ltx3drope_tables_t* out);

@@ -1,0 +1,95 @@
+"""GPU parity of patchify / unpatchify (through the C ABI) against oracle.patchify, bit for bit."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.patchify as pf
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+rla = pytest.importorskip("rope_ltx3drope_amd")
+from rope_ltx3drope_amd import _lib  # noqa: E402
+
+DEV = "cuda:0"
+TORCH_INT = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}
+NP_SIGNED = {1: np.uint8, 2: np.int16, 4: np.int32, 8: np.int64}
+
+
+@pytest.fixture(autouse=True)
+def fresh():
+    assert torch.cuda.is_available()
+    _lib.lib()
+    rla.set_option(rla.OPT_PATH, 0)
+    rla.stats_reset()
+    yield
+    rla.set_option(rla.OPT_PATH, 0)
+    torch.cuda.synchronize()
+
+
+def to_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x).view(NP_SIGNED[x.dtype.itemsize])).to(DEV)
+
+
+def to_host(t, like):
+    return t.cpu().numpy().view(like.dtype)
+
+
+@pytest.mark.parametrize("key", ["p1", "p2", "p3", "p4", "p5"])
+@pytest.mark.parametrize("path", [0, 2], ids=["fast", "plain"])
+def test_patchify_and_inverse_full(key, path):
+    shape, p, eb = workloads.PATCH_WORKLOADS[key]
+    x = workloads.generate_patch(shape, eb, seed=len(key) + p)
+    rla.set_option(rla.OPT_PATH, path)
+    y = rla.patchify(to_dev(x), p)
+    torch.cuda.synchronize()
+    want = pf.patchify(x, p)
+    np.testing.assert_array_equal(to_host(y, want), want)
+    back = rla.unpatchify(y, p)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(back, x), x)
+    yy = workloads.generate_patch(want.shape, eb, seed=7)
+    np.testing.assert_array_equal(to_host(rla.unpatchify(to_dev(yy), p), x), pf.unpatchify(yy, p))
+
+
+@pytest.mark.parametrize("eb", [1, 8])
+def test_other_element_sizes_use_the_plain_kernel(eb):
+    shape, p = (2, 3, 2, 12, 18), 3
+    x = workloads.generate_patch(shape, eb, seed=eb)
+    y = rla.patchify(to_dev(x), p)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(y, x), pf.patchify(x, p))
+    assert rla.stats()["plain_launches"] == 1 and rla.stats()["fast_launches"] == 0
+
+
+def test_full_clip_patchify_round_trip_in_full():
+    shape, p, eb = workloads.PATCH_WORKLOADS["p6"]
+    x = workloads.generate_patch(shape, eb, seed=6)
+    dx = to_dev(x)
+    y = rla.patchify(dx, p)
+    torch.cuda.synchronize()
+    want = pf.patchify(x, p)
+    assert np.array_equal(to_host(y, want), want)
+    del want
+    back = rla.unpatchify(y, p)
+    torch.cuda.synchronize()
+    assert torch.equal(back, dx)
+    assert rla.stats()["fast_launches"] == 2
+
+
+def test_refusals():
+    x = torch.zeros((1, 2, 1, 8, 8), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        rla.patchify(x, 3)
+    L = _lib.lib()
+    y = torch.empty((1, 8, 1, 4, 4), dtype=torch.bfloat16, device=DEV)
+    assert L.ltx3drope_patchify(y.data_ptr(), x.data_ptr(), 3, 1, 2, 1, 8, 8, 2, None) == _lib.E_INVALID
+    assert L.ltx3drope_patchify(y.data_ptr(), x.data_ptr(), 2, 1, 2, 1, 8, 0, 2, None) == _lib.E_INVALID
+    assert L.ltx3drope_patchify(x.data_ptr() + 2, x.data_ptr(), 2, 1, 2, 1, 8, 8, 2, None) == _lib.E_UNSUPPORTED
+    small = torch.empty(16, dtype=torch.bfloat16, device=DEV)
+    assert L.ltx3drope_patchify(y.data_ptr(), small.data_ptr(), 2, 1, 2, 1, 800, 800, 2, None) == _lib.E_UNSUPPORTED
+    host = torch.zeros((1, 2, 1, 8, 8), dtype=torch.bfloat16).pin_memory()
+    assert L.ltx3drope_patchify(y.data_ptr(), host.data_ptr(), 2, 1, 2, 1, 8, 8, 2, None) == _lib.E_UNSUPPORTED
+    assert rla.stats()["fast_launches"] == 0 and rla.stats()["plain_launches"] == 0

@@ -213,3 +213,25 @@ def generate_neox(w: NeoxWorkload):
     rows = np.concatenate([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
     cache = rows if w.cache_dtype == F32 else _f32_to_bf16_bits_torch(rows.reshape(-1)).reshape(rows.shape)
     return q, k, pos, cache
+
+
+# ---------------------------------------------------------------------------
+# stage-5 space-to-depth (patchify) inputs: (B, C, F, H, W) tensors of raw bits
+# ---------------------------------------------------------------------------
+
+PATCH_WORKLOADS = {
+    # key: (shape (B, C, F, H, W), p, element bytes)
+    "p1": ((1, 3, 5, 16, 24), 4, 4),        # W not a multiple of p*4 -> plain kernel
+    "p2": ((1, 3, 9, 64, 96), 4, 2),
+    "p3": ((2, 16, 5, 32, 48), 2, 2),
+    "p4": ((1, 3, 3, 64, 128), 8, 2),
+    "p5": ((1, 4, 7, 40, 80), 4, 4),
+    "p6": ((1, 3, 121, 544, 960), 4, 2),     # every frame of a 121 x 544 x 960 RGB clip, bf16
+}
+
+
+def generate_patch(shape, elem_bytes: int, seed: int) -> np.ndarray:
+    """Random bit patterns of the element width (the op moves data without reading values)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dt = {1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}[elem_bytes]
+    return rng.integers(0, np.iinfo(dt).max, size=shape, dtype=dt, endpoint=True)
