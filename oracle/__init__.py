@@ -16,7 +16,7 @@ sglang's own table bits is unpinned (no values are printed on the pages).
 oracle.neox: the rotate-half RoPE with a gathered cos/sin cache (pins in
 tests/test_neox_oracle_pins.py).
 """
-from . import neox, patchify  # noqa: F401
+from . import dit_freqs, neox, patchify  # noqa: F401
 from .rope import (  # noqa: F401
     BF16,
     F32,
