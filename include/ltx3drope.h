@@ -265,6 +265,42 @@ int ltx3drope_neox_apply_qk(void* q_out, void* k_out, const void* q, const void*
    `device`.  Synchronizes the device.  reset = 1 clears the count afterwards. */
 int ltx3drope_neox_position_errors(int device, int reset, int64_t* count);
 
+/*
+ * Stage-5 space-to-depth of the diffusion decoder (sglang PR #34471 page,
+ * "Key source snippets", _patchify) and its inverse (_unpatchify):
+ *     x (B, C, F, H, W) <-> y (B, C*p*p, F, H/p, W/p)
+ *     y[b, (c*p + pw)*p + ph, f, hh, ww] = x[b, c, f, hh*p + ph, ww*p + pw]
+ * i.e. channels packed as (channel, width offset, height offset).  Both tensors
+ * contiguous, elements of elem_bytes = 1, 2, 4 or 8 bytes (the op moves data
+ * and never looks at values, so it is exact for every dtype).  B, C, F, H, W
+ * are always the unpatched sizes.  E_INVALID: a size or p <= 0, H or W not a
+ * multiple of p, elem_bytes not 1/2/4/8, NULL pointers.  E_UNSUPPORTED: 2^31
+ * elements or more, pointers not aligned to one element, overlapping tensors,
+ * not device memory of one device, or allocations smaller than the tensors.
+ * Asynchronous on `stream`.
+ */
+int ltx3drope_patchify(void* y, const void* x, int elem_bytes, int64_t B, int64_t C, int64_t F, int64_t H,
+                       int64_t W, int64_t p, void* stream);
+int ltx3drope_unpatchify(void* x, const void* y, int elem_bytes, int64_t B, int64_t C, int64_t F, int64_t H,
+                         int64_t W, int64_t p, void* stream);
+
+/*
+ * LTX DiT RoPE frequency grid (sglang PR #24660 page, "Key source snippets",
+ * the DiT's frequency generation; "Implementation breakdown", step 2):
+ *     n = dim / num_rope_elems (integer division)
+ *     out[i] = float32( theta ** linspace(0, 1, n)[i] * pi / 2 )
+ * computed in float64 (double_precision = 1) or float32 (0).  linspace holds
+ * i / (n - 1) correctly rounded to the working dtype (0 for n = 1); in float32
+ * theta, the power and pi are each rounded to float32 and the product is an
+ * fp32 product.  Built on the host (libm); written to `out`, n floats, which is
+ * device memory when out_on_device = 1 (uploaded on `stream`, then that stream
+ * is synchronized) and host memory otherwise.  *count (if not NULL) receives n.
+ * E_INVALID: theta not finite or <= 0, dim < 0, num_rope_elems <= 0, n > 2^24,
+ * out NULL while n > 0.  E_HIP, E_NOMEM.
+ */
+int ltx3drope_dit_freq_grid(double theta, int64_t dim, int64_t num_rope_elems, int double_precision, float* out,
+                            int out_on_device, void* stream, int64_t* count);
+
 /* Gate state of one configuration key (LTX3DROPE_GATE_*), or a negative status. */
 int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W,
                          int64_t heads, int64_t head_dim, int64_t dim_t, int64_t dim_h, int64_t dim_w);

@@ -35,7 +35,7 @@ __all__ = [
     "Ltx3dRopeError", "Ltx3dRopeUnsupported", "Tables", "tables", "tables_build", "can_use", "apply_qk",
     "forward_pair", "kernel_choice", "stats", "stats_reset", "set_option", "get_option", "gate_state", "gate_reset",
     "cache_clear", "copy_bytes", "version", "neox_can_use", "neox_apply_qk", "neox_position_errors", "patchify",
-    "unpatchify",
+    "unpatchify", "dit_freq_grid",
 ]
 
 
@@ -359,6 +359,29 @@ def unpatchify(y, p: int, out=None, stream=None):
     if st == _lib.E_UNSUPPORTED:
         raise Ltx3dRopeUnsupported("PRECHECK", st)
     _check(st, "unpatchify")
+    return out
+
+
+def dit_freq_grid(theta: float, dim: int, num_rope_elems: int, double_precision: bool, device=None, stream=None):
+    """LTX DiT RoPE frequencies (float32, dim // num_rope_elems values): on `device` (a torch device)
+    when given, else as a numpy array."""
+    if int(num_rope_elems) <= 0:
+        raise ValueError("num_rope_elems must be positive")
+    count = max(0, int(dim) // int(num_rope_elems))
+    n = ctypes.c_int64(0)
+    args = (float(theta), int(dim), int(num_rope_elems), int(bool(double_precision)))
+    if device is None:
+        import numpy as np
+
+        out = np.empty(count, np.float32)
+        ptr = out.ctypes.data_as(ctypes.c_void_p) if count else None
+        _check(_lib.lib().ltx3drope_dit_freq_grid(*args, ptr, 0, None, ctypes.byref(n)), "dit_freq_grid")
+        return out
+    torch = _torch()
+    out = torch.empty(count, dtype=torch.float32, device=device)
+    ptr = out.data_ptr() if count else None
+    _check(_lib.lib().ltx3drope_dit_freq_grid(*args, ptr, 1, _stream_ptr(out.device, stream), ctypes.byref(n)),
+           "dit_freq_grid")
     return out
 
 

@@ -41,7 +41,8 @@ EXPORTS = (
     "ltx3drope_tables_build", "ltx3drope_tables_release", "ltx3drope_tables_describe", "ltx3drope_tables_read",
     "ltx3drope_cache_clear", "ltx3drope_can_use", "ltx3drope_apply_qk", "ltx3drope_can_use_shard",
     "ltx3drope_apply_qk_shard", "ltx3drope_neox_can_use", "ltx3drope_neox_apply_qk",
-    "ltx3drope_neox_position_errors", "ltx3drope_patchify", "ltx3drope_unpatchify", "ltx3drope_gate_state",
+    "ltx3drope_neox_position_errors", "ltx3drope_patchify", "ltx3drope_unpatchify", "ltx3drope_dit_freq_grid",
+    "ltx3drope_gate_state",
     "ltx3drope_gate_reset", "ltx3drope_set_option", "ltx3drope_get_option", "ltx3drope_stats",
     "ltx3drope_stats_reset", "ltx3drope_kernel_choice", "ltx3drope_copy", "ltx3drope_status_string",
     "ltx3drope_reason_string", "ltx3drope_version",
@@ -108,6 +109,8 @@ def lib() -> ctypes.CDLL:
             "ltx3drope_neox_position_errors": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.POINTER(i64)]),
             "ltx3drope_patchify": (ctypes.c_int, [vp, vp, ctypes.c_int] + [i64] * 6 + [vp]),
             "ltx3drope_unpatchify": (ctypes.c_int, [vp, vp, ctypes.c_int] + [i64] * 6 + [vp]),
+            "ltx3drope_dit_freq_grid": (ctypes.c_int, [ctypes.c_double, i64, i64, ctypes.c_int, vp, ctypes.c_int, vp,
+                                                       ctypes.POINTER(i64)]),
             "ltx3drope_gate_state": (ctypes.c_int, [ctypes.c_int, ctypes.c_int] + [i64] * 9),
             "ltx3drope_gate_reset": (ctypes.c_int, []),
             "ltx3drope_set_option": (ctypes.c_int, [ctypes.c_int, i64]),

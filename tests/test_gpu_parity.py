@@ -507,3 +507,13 @@ def test_inplace_matches_out_of_place_and_respects_the_gate(dtype):
         assert s["gate_verifications"] == 1 and s["fast_launches"] == 2
         assert_bitexact(to_host(dq, dtype), want_q, dtype, "q in place (fast)")
         assert_bitexact(to_host(dk, dtype), want_k, dtype, "k in place (fast)")
+
+
+def test_dit_freq_grid_on_device_equals_host():
+    import oracle.dit_freqs as df
+
+    for double in (True, False):
+        d = rla.dit_freq_grid(10000.0, 4096, 6, double, device=DEV)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(d.cpu().numpy().view(np.uint32),
+                                      df.freq_grid(10000.0, 4096, 6, double).view(np.uint32))
