@@ -517,3 +517,33 @@ def test_dit_freq_grid_on_device_equals_host():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(d.cpu().numpy().view(np.uint32),
                                       df.freq_grid(10000.0, 4096, 6, double).view(np.uint32))
+
+
+def test_largest_supported_tensor():
+    """15 heads x [1, 16, 64, 1024] x head_dim 128 = 2,013,265,920 elements per tensor, just under the
+    2^31 limit: the gate's full-size verification, fast == plain over the whole output, sampled
+    tokens against the oracle; one more head (2^31 elements) is refused without a launch."""
+    shape, split = (1, 16, 64, 1024, 15, 128), (32, 48, 48)
+    log("largest tensor: generating inputs")
+    q = workloads.generate_bf16_bits(shape, 101)
+    k = workloads.generate_bf16_bits(shape, 102)
+    dq, dk = to_dev(q, oracle.BF16), to_dev(k, oracle.BF16)
+    with rla.tables_build(16, 64, 1024, split) as tab:
+        too_big = (1, 16, 64, 1024, 16, 128)
+        reason = ctypes.c_int(0)
+        assert _lib.lib().ltx3drope_can_use(None, None, dq.data_ptr(), dk.data_ptr(), _lib.DTYPE_BF16, *too_big,
+                                            tab.handle, ctypes.byref(reason)) == 0
+        assert _lib.REASONS[reason.value] == "TOO_LARGE"
+        qo, ko = rla.apply_qk(dq, dk, tab)  # first call: fast kernel verified against the plain one
+        torch.cuda.synchronize()
+        assert rla.gate_state(0, rla.DTYPE_BF16, shape, split) == "TRUSTED"
+        rla.set_option(rla.OPT_PATH, 2)
+        pq, pk = rla.apply_qk(dq, dk, tab)
+        torch.cuda.synchronize()
+        assert torch.equal(qo.view(torch.int16), pq.view(torch.int16))
+        assert torch.equal(ko.view(torch.int16), pk.view(torch.int16))
+        del pq, pk
+    w = workloads.Workload(0, "largest", oracle.BF16, 1, ((16, 64, 1024),), 15, 128, split, 10000.0, 0, "bits", (0,))
+    log("largest tensor: sampled oracle comparison")
+    sampled_check(q, qo, w, 0, 800, seed=90)
+    sampled_check(k, ko, w, 0, 800, seed=91)

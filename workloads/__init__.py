@@ -135,6 +135,19 @@ def generate(w: Workload, grid_indices: Sequence[int] | None = None) -> List[Tup
     return out
 
 
+def generate_bf16_bits(shape: Sequence[int], seed: int) -> np.ndarray:
+    """Finite bf16 bit patterns of random sign and mantissa with magnitudes in [1/8, 2): a cheap
+    generator for the largest tensors (billions of elements), where normal draws would take minutes."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, _CHUNK * 4):
+        e = min(n, s + _CHUNK * 4)
+        raw = rng.integers(0, 1 << 16, size=e - s, dtype=np.uint16)
+        out[s:e] = (raw & np.uint16(0x81FF)) | np.uint16(0x3E00)  # exponent field 0x7C..0x7F
+    return out.reshape(shape)
+
+
 def generate_custom(shape: Sequence[int], dtype: str, seed: int, scale: float | None = None):
     """Q, K of an arbitrary [B,T,H,W,heads,D] shape with N(0,1)*scale values (tests)."""
     rng = np.random.Generator(np.random.PCG64(seed))
