@@ -35,6 +35,7 @@
 #include <mutex>
 
 #include "internal.h"
+#include "stream_store.h"
 
 #pragma clang fp contract(off)
 
@@ -204,9 +205,10 @@ struct FastArgs {
 // once per wavefront on wave-uniform (scalar) values.  Otherwise each lane
 // decodes its own token.
 //
-// Q and K are read and the results written with non-temporal hints: every byte
-// is touched exactly once, so the streams should not displace other data from
-// the caches (measured: +3 to +10 % on the 0.8-6.8 GB workloads).
+// Q and K are read with non-temporal hints and the results written with the
+// streaming store (sc1 | nt): every byte is touched exactly once, so the streams
+// should not displace other data from the caches (measured: +3 to +10 % on the
+// 0.8-6.8 GB workloads for the hints, about +1 % more for the store policy).
 template <bool BF16, bool WAVE_TOKEN>
 __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
     constexpr uint32_t PPV = BF16 ? 4 : 2;
@@ -262,7 +264,7 @@ __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
         rotate(__uint_as_float(x.z), __uint_as_float(x.w), cs0.z, cs0.w, y2, y3);
         y = (u32x4){__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
     }
-    __builtin_nontemporal_store(y, dst + g);
+    stream_store16(y, dst + blk * kFastBlock, kFastBlock * 16u, threadIdx.x * 16u);
 }
 
 // ---------------------------------------------------------------------------
@@ -277,7 +279,7 @@ __global__ void zero_u32(unsigned* p) {
 // read stream and one write stream.
 __global__ void __launch_bounds__(kFastBlock) copy16(u32x4* __restrict__ dst, const u32x4* __restrict__ src, uint32_t n) {
     const uint32_t i = blockIdx.x * kFastBlock + threadIdx.x;
-    if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    if (i < n) stream_store16(__builtin_nontemporal_load(src + i), dst + blockIdx.x * kFastBlock, kFastBlock * 16u, threadIdx.x * 16u);
 }
 
 // ---------------------------------------------------------------------------

@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
+#include "stream_store.h"
 
 #pragma clang fp contract(off)
 
@@ -146,10 +147,14 @@ __global__ void __launch_bounds__(kBlock) neox_fast(NeoxArgs a) {
     } else if (hs == 0 && v == 0) {
         atomicAdd(a.errors, 1u);
     }
+    const uint32_t token_bytes = heads * a.D * es;  // below 2^31: checked on the host
+    char* const dst_tok = dst + static_cast<size_t>(tok) * token_bytes;  // wave-uniform
     for (uint32_t head = hs; head < heads; head += hpw) {
         const size_t row = (static_cast<size_t>(tok) * heads + head) * a.D;  // element offset of the head row
         const size_t off1 = (row + static_cast<size_t>(v) * E) * es;
         const size_t off2 = off1 + static_cast<size_t>(a.D / 2) * es;
+        const uint32_t in_tok1 = (head * a.D + v * E) * es;  // off1 - tok * token_bytes
+        const uint32_t in_tok2 = in_tok1 + (a.D / 2) * es;
         const u32x4 x1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off1));
         const u32x4 x2 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off2));
         u32x4 y1, y2;
@@ -187,8 +192,8 @@ __global__ void __launch_bounds__(kBlock) neox_fast(NeoxArgs a) {
                 y2[j] = __float_as_uint(__fadd_rn(__fmul_rn(e2, c[j]), __fmul_rn(e1, s[j])));
             }
         }
-        __builtin_nontemporal_store(y1, reinterpret_cast<u32x4*>(dst + off1));
-        __builtin_nontemporal_store(y2, reinterpret_cast<u32x4*>(dst + off2));
+        stream_store16(y1, dst_tok, token_bytes, in_tok1);
+        stream_store16(y2, dst_tok, token_bytes, in_tok2);
     }
 }
 
@@ -284,6 +289,8 @@ bool neox_fast_supported(const NeoxProblem& p) {
     const uint32_t es = p.dtype == LTX3DROPE_DTYPE_F32 ? 4u : 2u;
     for (const void* ptr : {p.q, p.k, static_cast<const void*>(p.q_out), static_cast<const void*>(p.k_out), p.cache})
         if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return false;
+    const uint64_t heads = p.q_heads > p.k_heads ? p.q_heads : p.k_heads;
+    if (heads * p.D * es >= (uint64_t(1) << 31)) return false;  // a token's row is addressed with 32-bit offsets
     return (p.D / 2 * es) % 16 == 0 && p.D / 2 * es / 16 <= 64;
 }
 
