@@ -8,24 +8,29 @@
 // movement, so the result is bit-exact for any element type; the kernels move
 // elements of 1, 2, 4 or 8 bytes.
 //
-//  * patch_fast<T, P>: one thread per group of P consecutive 16-byte vectors of
-//    an input row (P * E elements, E = 16 / sizeof(T)).  Those elements feed P
-//    output rows (one per width offset) with E consecutive elements each, so
-//    the thread transposes P x E elements in registers and writes P 16-byte
-//    vectors.  Used for patchify, and for the inverse when a vector does not
-//    split evenly across the P width offsets.  Needs W to be a multiple of
-//    P * E and 16-byte aligned tensors.
-//  * unpatch_gather<T, P>: the inverse with one unpatched 16-byte vector per
-//    thread and P loads of E/P packed elements.
-//  * patch_plain<T, INVERSE>: one element per thread, any shape.
-// Threads are ordered (b, c, f, height offset, patch row, vector) rather than
-// by input row: a wavefront then writes (patchify) or reads (unpatchify)
-// consecutive rows of one packed plane, whose rows of W/p elements are not
-// whole cache lines.  Measured on a 121-frame 544 x 960 bf16 clip, p = 4:
-// patchify 5.5 TB/s against 4.1 TB/s in input-row order; unpatchify 5.9 TB/s
-// (with non-temporal hints, which help only once every instruction is
-// contiguous).  The register-transpose kernel keeps plain loads and stores:
-// with non-temporal hints it measured slower.
+//  * patch_lds<T, P> / unpatch_lds<T, P>: a wavefront owns P*64 consecutive
+//    16-byte vectors of the unpatched tensor, taken in (b, c, f, height offset,
+//    patch row, vector) order, which are exactly 64 consecutive packed vectors of
+//    each of the P width-offset planes that share (b, c, height offset).  The
+//    wavefront reads one side with P contiguous 1 KB loads, regroups the
+//    elements by width offset through P KB of LDS, and writes the other side
+//    with P contiguous 1 KB stores.  Used whenever a 16-byte
+//    vector splits evenly across the P width offsets (16/sizeof(T) a multiple
+//    of p: bf16 with p = 2, 4, 8; fp32 with p = 2, 4).
+//  * patch_fast<T, P, INVERSE>: one thread per group of P consecutive 16-byte
+//    vectors of an unpatched row, transposed in registers; covers the remaining
+//    fast case (fp32, p = 8), in both directions.
+//  * patch_plain<T, INVERSE>: one element per thread, any shape and element
+//    size (1, 2, 4 or 8 bytes).
+// The fast kernels need W to be a multiple of p * 16/sizeof(T) and 16-byte
+// aligned tensors.
+//
+// Measured on MI355X on a 121-frame 544 x 960 bf16 clip, p = 4 (758 MB moved):
+// threads in unpatched-row order wrote each 480-byte packed row piecemeal
+// (4.1 TB/s); the (b, c, f, height offset, patch row) order with a register
+// transpose reached 5.5 TB/s (patchify) and a per-lane gather 6.0 TB/s
+// (unpatchify); the LDS-staged kernels, whose every global instruction is a
+// contiguous 1 KB, reach 5.9 and 6.2 TB/s with non-temporal loads and stores.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -47,7 +52,7 @@ struct PatchArgs {
     void* dst;
     uint32_t B, C, F, H, W, p;
     uint32_t groups_per_row;  // fast kernel: W / (P * E)
-    uint32_t groups;          // fast kernel: B*C*F*H*groups_per_row
+    uint32_t groups;          // patch_fast: B*C*F*H*groups_per_row; LDS kernels: 16-byte vectors of the unpatched tensor
     uint64_t numel;           // plain kernel
 };
 
@@ -115,14 +120,50 @@ __global__ void __launch_bounds__(kBlock) patch_fast(PatchArgs a) {
     }
 }
 
-// Inverse with one 16-byte vector of the unpatched tensor per thread (E elements,
-// columns E*vi .. E*vi + E - 1 of one row): for each width offset pw it loads the
-// K = E / P consecutive packed elements at patch columns K*vi .. K*vi + K - 1,
-// then interleaves them.  Consecutive lanes touch consecutive addresses in every
-// load (K elements each) and store (16 bytes each), so every instruction is
-// contiguous across the wavefront.
+// (b*C + c, f, height offset, patch row) of row `rowid` in (b, c, f, height offset, patch row) order.
+struct RowId {
+    uint32_t bc, f, ph, hh;
+};
+
+template <int P>
+__device__ __forceinline__ RowId decode_row(uint32_t rowid, uint32_t Hp, uint32_t F) {
+    RowId d;
+    d.hh = rowid % Hp;
+    const uint32_t t = rowid / Hp;
+    d.ph = t % P;
+    const uint32_t bcf = t / P;
+    d.bc = bcf / F;
+    d.f = bcf - d.bc * F;
+    return d;
+}
+
+// Element offset of unpatched vector I (16-byte vectors in (b, c, f, ph, hh, x) order).
+template <int P, int E>
+__device__ __forceinline__ uint64_t unpatched_offset(const PatchArgs& a, uint32_t I) {
+    const uint32_t WE = a.W / E;
+    const uint32_t rowid = I / WE;
+    const uint32_t x = I - rowid * WE;
+    const RowId d = decode_row<P>(rowid, a.H / P, a.F);
+    const uint64_t row = (static_cast<uint64_t>(d.bc) * a.F + d.f) * a.H + d.hh * P + d.ph;
+    return row * a.W + static_cast<uint64_t>(x) * E;
+}
+
+// Element offset of packed vector O of the width-offset-0 plane (packed vectors in the same
+// order); the plane of width offset pw lies pw * P * F * (H/P) * (W/P) elements further.
+template <int P, int E>
+__device__ __forceinline__ uint64_t packed_offset0(const PatchArgs& a, uint32_t O) {
+    const uint32_t Hp = a.H / P, Wp = a.W / P;
+    const uint32_t WpE = Wp / E;
+    const uint32_t rowid = O / WpE;
+    const uint32_t wv = O - rowid * WpE;
+    const RowId d = decode_row<P>(rowid, Hp, a.F);
+    const uint64_t co = static_cast<uint64_t>(d.bc) * P * P + d.ph;  // output channel of width offset 0
+    return ((co * a.F + d.f) * Hp + d.hh) * Wp + static_cast<uint64_t>(wv) * E;
+}
+
+// One chunk of K = E/P elements: the elements of one 16-byte vector that share a width offset.
 template <int NB>
-struct Chunk;  // a naturally aligned chunk of NB bytes
+struct Chunk;
 template <>
 struct Chunk<2> { typedef uint16_t type; };
 template <>
@@ -130,44 +171,91 @@ struct Chunk<4> { typedef uint32_t type; };
 template <>
 struct Chunk<8> { typedef unsigned type __attribute__((ext_vector_type(2))); };
 
+// Wavefront w owns unpatched vectors [w*P*64, (w+1)*P*64) and packed vectors
+// [w*64, (w+1)*64) of every width-offset plane.  Unpatched vector I holds, for each
+// width offset pw, K elements at consecutive packed positions; element k*P + pw of the
+// wavefront's local vector li goes to lds[pw][li*K + k].  Lane l then owns packed vector
+// w*64 + l, which is lds[pw][l*E .. l*E + E - 1].
 template <typename T, int P>
-__global__ void __launch_bounds__(kBlock) unpatch_gather(PatchArgs a) {
+__global__ void __launch_bounds__(kBlock) patch_lds(PatchArgs a) {
     constexpr int E = 16 / sizeof(T);
-    constexpr int K = E / P;  // packed elements per width offset
-    static_assert(K * P == E && K >= 1, "a vector must split evenly across the width offsets");
-    typedef typename Chunk<K * sizeof(T)>::type C;
-    const uint32_t g = blockIdx.x * kBlock + threadIdx.x;
-    if (g >= a.groups) return;  // here: 16-byte vectors of the unpatched tensor
-    // thread order (b, c, f, ph, hh, vi): consecutive threads read consecutive packed
-    // elements of one plane, across its rows
-    const uint32_t vpr = a.W / E;
-    uint32_t t = g / vpr;
-    const uint32_t vi = g - t * vpr;
-    const uint32_t Hp = a.H / P;
-    const uint32_t hh = t % Hp;
-    t /= Hp;
-    const uint32_t ph = t % P;
-    t /= P;
-    const uint32_t f = t % a.F;
-    t /= a.F;
-    const uint32_t c = t % a.C;
-    const uint32_t b = t / a.C;
-    const uint64_t row = ((static_cast<uint64_t>(b) * a.C + c) * a.F + f) * a.H + hh * P + ph;
+    constexpr int K = E / P;
+    static_assert(K * P == E, "a vector must split evenly across the width offsets");
+    typedef typename Chunk<K * sizeof(T)>::type Ch;
+    __shared__ __align__(16) T lds[P][kBlock * E];
+    const uint32_t lane = threadIdx.x;
+    const uint32_t first = blockIdx.x * (P * kBlock);
     const T* src = static_cast<const T*>(a.src);
-    Vec<T> seg[P];
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+        const uint32_t I = first + r * kBlock + lane;
+        if (I >= a.groups) break;  // the tail: nothing later in this lane is valid either
+        const Vec<T> v = __builtin_bit_cast(
+            Vec<T>, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + unpatched_offset<P, E>(a, I))));
+        const uint32_t li = r * kBlock + lane;
+#pragma unroll
+        for (int pw = 0; pw < P; ++pw) {
+            T ch[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) ch[k] = v.e[k * P + pw];
+            Ch c;
+            __builtin_memcpy(&c, ch, sizeof(Ch));
+            reinterpret_cast<Ch*>(&lds[pw][0])[li] = c;
+        }
+    }
+    __syncthreads();
+    const uint32_t O = blockIdx.x * kBlock + lane;
+    if (O >= a.groups / P) return;
+    const uint64_t off0 = packed_offset0<P, E>(a, O);
+    const uint64_t plane_stride = static_cast<uint64_t>(P) * a.F * (a.H / P) * (a.W / P);
+    T* dst = static_cast<T*>(a.dst);
 #pragma unroll
     for (int pw = 0; pw < P; ++pw) {
-        const C v = __builtin_nontemporal_load(
-            reinterpret_cast<const C*>(src + packed_offset(a, b, c, pw, ph, f, hh, vi * K)));
-        Vec<T> piece{};
-        __builtin_memcpy(&piece.e[0], &v, sizeof(C));  // the first K elements
-        seg[pw] = piece;
+        const u32x4 o = reinterpret_cast<const u32x4*>(&lds[pw][0])[lane];
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + off0 + pw * plane_stride));
     }
-    Vec<T> o;
+}
+
+// The inverse: the wavefront reads its 64 packed vectors of each width-offset plane into
+// lds[pw], then assembles its P*64 unpatched vectors.
+template <typename T, int P>
+__global__ void __launch_bounds__(kBlock) unpatch_lds(PatchArgs a) {
+    constexpr int E = 16 / sizeof(T);
+    constexpr int K = E / P;
+    static_assert(K * P == E, "a vector must split evenly across the width offsets");
+    typedef typename Chunk<K * sizeof(T)>::type Ch;
+    __shared__ __align__(16) T lds[P][kBlock * E];
+    const uint32_t lane = threadIdx.x;
+    const uint32_t O = blockIdx.x * kBlock + lane;
+    const T* src = static_cast<const T*>(a.src);
+    if (O < a.groups / P) {
+        const uint64_t off0 = packed_offset0<P, E>(a, O);
+        const uint64_t plane_stride = static_cast<uint64_t>(P) * a.F * (a.H / P) * (a.W / P);
 #pragma unroll
-    for (int j = 0; j < E; ++j) o.e[j] = seg[j % P].e[j / P];
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o),
-                                reinterpret_cast<u32x4*>(static_cast<T*>(a.dst) + row * a.W) + vi);
+        for (int pw = 0; pw < P; ++pw)
+            reinterpret_cast<u32x4*>(&lds[pw][0])[lane] =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off0 + pw * plane_stride));
+    }
+    __syncthreads();
+    const uint32_t first = blockIdx.x * (P * kBlock);
+    T* dst = static_cast<T*>(a.dst);
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+        const uint32_t I = first + r * kBlock + lane;
+        if (I >= a.groups) break;
+        const uint32_t li = r * kBlock + lane;
+        Vec<T> v;
+#pragma unroll
+        for (int pw = 0; pw < P; ++pw) {
+            const Ch c = reinterpret_cast<const Ch*>(&lds[pw][0])[li];
+            T ch[K];
+            __builtin_memcpy(ch, &c, sizeof(Ch));
+#pragma unroll
+            for (int k = 0; k < K; ++k) v.e[k * P + pw] = ch[k];
+        }
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                    reinterpret_cast<u32x4*>(dst + unpatched_offset<P, E>(a, I)));
+    }
 }
 
 template <typename T, bool INVERSE>
@@ -222,6 +310,30 @@ hipError_t launch_plain_t(PatchArgs a, uint32_t elem_bytes, hipStream_t stream, 
     return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_lds_t(PatchArgs a, uint32_t P, bool inverse, uint32_t blocks, hipStream_t stream) {
+    constexpr uint32_t E = 16 / sizeof(T);
+    switch (P) {
+        case 2:
+            if (inverse) hipLaunchKernelGGL((unpatch_lds<T, 2>), dim3(blocks), dim3(kBlock), 0, stream, a);
+            else hipLaunchKernelGGL((patch_lds<T, 2>), dim3(blocks), dim3(kBlock), 0, stream, a);
+            break;
+        case 4:
+            if (inverse) hipLaunchKernelGGL((unpatch_lds<T, 4>), dim3(blocks), dim3(kBlock), 0, stream, a);
+            else hipLaunchKernelGGL((patch_lds<T, 4>), dim3(blocks), dim3(kBlock), 0, stream, a);
+            break;
+        case 8:
+            if constexpr (E % 8 == 0) {
+                if (inverse) hipLaunchKernelGGL((unpatch_lds<T, 8>), dim3(blocks), dim3(kBlock), 0, stream, a);
+                else hipLaunchKernelGGL((patch_lds<T, 8>), dim3(blocks), dim3(kBlock), 0, stream, a);
+                break;
+            }
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool patch_fast_supported(const PatchProblem& p) {
@@ -248,18 +360,11 @@ hipError_t launch_patch(const PatchProblem& p, bool inverse, hipStream_t stream,
     if (a.numel == 0) return hipSuccess;
     if (patch_fast_supported(p) && !p.force_plain) {
         const uint32_t E = 16 / p.elem_bytes;
-        if (inverse && E % p.p == 0) {
-            a.groups = static_cast<uint32_t>(a.numel / E);  // one unpatched 16-byte vector per thread
-            const uint32_t blocks = (a.groups + kBlock - 1) / kBlock;
-            if (p.elem_bytes == 2) {
-                if (p.p == 2) hipLaunchKernelGGL((unpatch_gather<uint16_t, 2>), dim3(blocks), dim3(kBlock), 0, stream, a);
-                else if (p.p == 4) hipLaunchKernelGGL((unpatch_gather<uint16_t, 4>), dim3(blocks), dim3(kBlock), 0, stream, a);
-                else hipLaunchKernelGGL((unpatch_gather<uint16_t, 8>), dim3(blocks), dim3(kBlock), 0, stream, a);
-            } else {
-                if (p.p == 2) hipLaunchKernelGGL((unpatch_gather<uint32_t, 2>), dim3(blocks), dim3(kBlock), 0, stream, a);
-                else hipLaunchKernelGGL((unpatch_gather<uint32_t, 4>), dim3(blocks), dim3(kBlock), 0, stream, a);
-            }
-            return hipGetLastError();
+        if (E % p.p == 0) {
+            a.groups = static_cast<uint32_t>(a.numel / E);  // 16-byte vectors of the unpatched tensor
+            const uint32_t blocks = (a.groups + p.p * kBlock - 1) / (p.p * kBlock);
+            return p.elem_bytes == 2 ? launch_lds_t<uint16_t>(a, p.p, inverse, blocks, stream)
+                                     : launch_lds_t<uint32_t>(a, p.p, inverse, blocks, stream);
         }
         a.groups_per_row = p.W / (p.p * E);
         a.groups = static_cast<uint32_t>(a.numel / (p.p * E));

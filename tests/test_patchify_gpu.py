@@ -37,12 +37,13 @@ def to_host(t, like):
     return t.cpu().numpy().view(like.dtype)
 
 
-@pytest.mark.parametrize("key", ["p1", "p2", "p3", "p4", "p5"])
+@pytest.mark.parametrize("key", ["p1", "p2", "p3", "p4", "p5", "p7", "p8", "p9", "p10", "p11"])
 @pytest.mark.parametrize("path", [0, 2], ids=["fast", "plain"])
 def test_patchify_and_inverse_full(key, path):
     shape, p, eb = workloads.PATCH_WORKLOADS[key]
     x = workloads.generate_patch(shape, eb, seed=len(key) + p)
     rla.set_option(rla.OPT_PATH, path)
+    fast = path == 0 and shape[4] % (p * 16 // eb) == 0  # the library's rule for its fast kernels
     y = rla.patchify(to_dev(x), p)
     torch.cuda.synchronize()
     want = pf.patchify(x, p)
@@ -52,6 +53,8 @@ def test_patchify_and_inverse_full(key, path):
     np.testing.assert_array_equal(to_host(back, x), x)
     yy = workloads.generate_patch(want.shape, eb, seed=7)
     np.testing.assert_array_equal(to_host(rla.unpatchify(to_dev(yy), p), x), pf.unpatchify(yy, p))
+    st = rla.stats()
+    assert (st["fast_launches"], st["plain_launches"]) == ((3, 0) if fast else (0, 3))
 
 
 @pytest.mark.parametrize("eb", [1, 8])

@@ -240,6 +240,11 @@ PATCH_WORKLOADS = {
     "p4": ((1, 3, 3, 64, 128), 8, 2),
     "p5": ((1, 4, 7, 40, 80), 4, 4),
     "p6": ((1, 3, 121, 544, 960), 4, 2),     # every frame of a 121 x 544 x 960 RGB clip, bf16
+    "p7": ((1, 2, 3, 6, 48), 2, 2),          # bf16, p = 2, last wavefront partly filled
+    "p8": ((1, 3, 5, 8, 40), 2, 4),          # fp32, p = 2, last wavefront partly filled
+    "p9": ((1, 2, 3, 16, 64), 8, 4),         # fp32, p = 8: a vector does not split across 8 offsets
+    "p10": ((1, 1, 3, 24, 192), 8, 2),       # bf16, p = 8, last wavefront partly filled
+    "p11": ((1, 5, 1, 4, 64), 4, 2),         # bf16, p = 4, one partly filled wavefront
 }
 
 
