@@ -94,6 +94,7 @@ void gate_set(const GateKey& key, int s) {
 struct DeviceRes {
     unsigned* counter = nullptr;  // [0]: mismatches of the gate's verification, [1]: out-of-cache positions
     int cu_count = 0;
+    std::mutex verify_mu;  // one gate verification at a time per device: they share counter[0]
 };
 
 std::mutex g_dev_mu;
@@ -288,6 +289,9 @@ int verify_fast(const Problem& p, hipStream_t stream, int device, bool* equal) {
     DeviceRes* res = nullptr;
     int st = device_res(device, &res);
     if (st != LTX3DROPE_OK) return st;
+    // held until the count is back on the host, so concurrent first calls (other threads, other
+    // streams) cannot clear or add to this verification's counter
+    std::lock_guard<std::mutex> lock(res->verify_mu);
     st = run_kernel(Kernel::Fast, p, stream, device);
     if (st != LTX3DROPE_OK) return st;
     if (launch_zero_u32(res->counter, stream) != hipSuccess) return LTX3DROPE_E_HIP;

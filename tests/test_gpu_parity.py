@@ -416,6 +416,43 @@ def test_side_stream_and_forward_pair():
     assert_bitexact(to_host(ko, oracle.BF16), want_k, oracle.BF16, "k")
 
 
+def test_concurrent_first_calls_from_threads():
+    """First calls of four new configurations started together from host threads, each on its own
+    stream: the gate's verifications share one device counter and must not disturb each other."""
+    import threading
+    cases = [((1, 2, 4, 4, 8, 64), (16, 24, 24)), ((1, 3, 4, 6, 4, 96), (32, 32, 32)),
+             ((2, 2, 3, 5, 6, 64), (16, 16, 32)), ((1, 4, 2, 8, 8, 128), (32, 48, 48))]
+    inputs = [workloads.generate_custom(shape, oracle.BF16, seed=30 + i) for i, (shape, _) in enumerate(cases)]
+    dev_in = [(to_dev(q, oracle.BF16), to_dev(k, oracle.BF16)) for q, k in inputs]
+    streams = [torch.cuda.Stream() for _ in cases]
+    torch.cuda.synchronize()
+    results, errors = [None] * len(cases), []
+    start = threading.Barrier(len(cases))
+
+    def worker(i):
+        try:
+            start.wait(timeout=60)
+            with torch.cuda.stream(streams[i]):
+                results[i] = rla.forward_pair(*dev_in[i], cases[i][1])
+            streams[i].synchronize()
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    for i, (shape, split) in enumerate(cases):
+        want_q, want_k = oracle.rope3d_qk(*inputs[i], oracle.BF16, split)
+        assert_bitexact(to_host(results[i][0], oracle.BF16), want_q, oracle.BF16, f"q{i}")
+        assert_bitexact(to_host(results[i][1], oracle.BF16), want_k, oracle.BF16, f"k{i}")
+        assert rla.gate_state(0, rla.DTYPE_BF16, shape, split) == "TRUSTED"
+    s = rla.stats()
+    assert s["gate_verifications"] == len(cases) and s["gate_disabled"] == 0
+
+
 def test_copy_helper():
     src = torch.randint(-1000, 1000, (1 << 20,), dtype=torch.int32, device=DEV)
     dst = torch.empty_like(src)

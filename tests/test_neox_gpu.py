@@ -97,6 +97,10 @@ SHAPES = [
     (oracle.F32, 17, 2, 1, 16, 9, oracle.BF16),
     (oracle.F32, 5, 1, 1, 2, 3, oracle.F32),
     (oracle.BF16, 300, 16, 8, 256, 512, oracle.BF16),
+    # more head rows per lane than one batch of four: 3 and 2 batches, the last partial
+    (oracle.BF16, 50, 40, 24, 256, 100, oracle.F32),
+    (oracle.F32, 33, 12, 5, 256, 64, oracle.BF16),   # 2 head slots per wavefront, uneven K rows
+    (oracle.BF16, 11, 100, 7, 48, 20, oracle.BF16),  # 21 head slots, one lane idle
 ]
 
 
