@@ -30,10 +30,12 @@
 // (4.1 TB/s); the (b, c, f, height offset, patch row) order with a register
 // transpose reached 5.5 TB/s (patchify) and a per-lane gather 6.0 TB/s
 // (unpatchify); the LDS-staged kernels, whose every global instruction is a
-// contiguous 1 KB, reach 5.9 and 6.2 TB/s with non-temporal loads and stores.
+// contiguous 1 KB, reach 5.9 and 6.2 TB/s with non-temporal loads and
+// streaming (sc1 | nt) stores.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
+#include "stream_store.h"
 
 namespace ltx3drope {
 namespace {
@@ -54,7 +56,19 @@ struct PatchArgs {
     uint32_t groups_per_row;  // fast kernel: W / (P * E)
     uint32_t groups;          // patch_fast: B*C*F*H*groups_per_row; LDS kernels: 16-byte vectors of the unpatched tensor
     uint64_t numel;           // plain kernel
+    uint32_t dst_bytes;       // LDS kernels: output size in bytes when below 2^31 (streaming stores), else 0
 };
+
+// LDS kernels' 16-byte store at element offset `off` of the output: a streaming store (sc1 | nt)
+// relative to the output's base when its size fits the 32-bit offset, else a global store with
+// the non-temporal hint.  dst_bytes is uniform, so the branch is too.
+template <typename T>
+__device__ __forceinline__ void store_out(const PatchArgs& a, uint64_t off, u32x4 v) {
+    if (a.dst_bytes != 0)
+        stream_store16(v, a.dst, a.dst_bytes, static_cast<uint32_t>(off * sizeof(T)));
+    else
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<T*>(a.dst) + off));
+}
 
 // Element offset of output channel (c*p + pw)*p + ph, frame f, patch row hh, column ww.
 __device__ __forceinline__ uint64_t packed_offset(const PatchArgs& a, uint32_t b, uint32_t c, uint32_t pw,
@@ -208,11 +222,10 @@ __global__ void __launch_bounds__(kBlock) patch_lds(PatchArgs a) {
     if (O >= a.groups / P) return;
     const uint64_t off0 = packed_offset0<P, E>(a, O);
     const uint64_t plane_stride = static_cast<uint64_t>(P) * a.F * (a.H / P) * (a.W / P);
-    T* dst = static_cast<T*>(a.dst);
 #pragma unroll
     for (int pw = 0; pw < P; ++pw) {
         const u32x4 o = reinterpret_cast<const u32x4*>(&lds[pw][0])[lane];
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + off0 + pw * plane_stride));
+        store_out<T>(a, off0 + pw * plane_stride, o);
     }
 }
 
@@ -238,7 +251,6 @@ __global__ void __launch_bounds__(kBlock) unpatch_lds(PatchArgs a) {
     }
     __syncthreads();
     const uint32_t first = blockIdx.x * (P * kBlock);
-    T* dst = static_cast<T*>(a.dst);
 #pragma unroll
     for (int r = 0; r < P; ++r) {
         const uint32_t I = first + r * kBlock + lane;
@@ -253,8 +265,7 @@ __global__ void __launch_bounds__(kBlock) unpatch_lds(PatchArgs a) {
 #pragma unroll
             for (int k = 0; k < K; ++k) v.e[k * P + pw] = ch[k];
         }
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
-                                    reinterpret_cast<u32x4*>(dst + unpatched_offset<P, E>(a, I)));
+        store_out<T>(a, unpatched_offset<P, E>(a, I), __builtin_bit_cast(u32x4, v));
     }
 }
 
@@ -357,6 +368,8 @@ hipError_t launch_patch(const PatchProblem& p, bool inverse, hipStream_t stream,
     a.numel = static_cast<uint64_t>(p.B) * p.C * p.F * p.H * p.W;
     a.groups_per_row = 0;
     a.groups = 0;
+    const uint64_t bytes = static_cast<uint64_t>(p.B) * p.C * p.F * p.H * p.W * p.elem_bytes;
+    a.dst_bytes = bytes < (uint64_t(1) << 31) ? static_cast<uint32_t>(bytes) : 0u;
     if (a.numel == 0) return hipSuccess;
     if (patch_fast_supported(p) && !p.force_plain) {
         const uint32_t E = 16 / p.elem_bytes;

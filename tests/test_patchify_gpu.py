@@ -96,3 +96,34 @@ def test_refusals():
     host = torch.zeros((1, 2, 1, 8, 8), dtype=torch.bfloat16).pin_memory()
     assert L.ltx3drope_patchify(y.data_ptr(), host.data_ptr(), 2, 1, 2, 1, 8, 8, 2, None) == _lib.E_UNSUPPORTED
     assert rla.stats()["fast_launches"] == 0 and rla.stats()["plain_launches"] == 0
+
+
+def test_output_of_2_gib_or_more():
+    """An output of 2^31 bytes or more (the LDS kernels then store with 64-bit addresses instead of
+    32-bit offsets from the output's base): whole-tensor fast == plain and round trip on the
+    device, sampled frames against the oracle."""
+    shape, p = (1, 8, 129, 1088, 960), 4
+    B, C, F, H, W = shape
+    assert B * C * F * H * W * 2 >= 2 ** 31 and B * C * F * H * W < 2 ** 31
+    g = torch.Generator(device=DEV)
+    g.manual_seed(123)
+    x = torch.randint(-32768, 32767, shape, dtype=torch.int16, device=DEV, generator=g)
+    y = rla.patchify(x, p)
+    rla.set_option(rla.OPT_PATH, 2)
+    y_plain = rla.patchify(x, p)
+    rla.set_option(rla.OPT_PATH, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_plain)
+    del y_plain
+    back = rla.unpatchify(y, p)
+    torch.cuda.synchronize()
+    assert torch.equal(back, x)
+    del back
+    rng = np.random.default_rng(5)
+    for c, f in zip(rng.integers(0, C, 6), rng.integers(0, F, 6)):
+        frame = x[0:1, c:c + 1, f:f + 1].cpu().numpy()
+        want = pf.patchify(frame, p)[0, :, 0]
+        got = y[0, c * p * p:(c + 1) * p * p, f].cpu().numpy()
+        np.testing.assert_array_equal(got, want)
+    st = rla.stats()
+    assert st["fast_launches"] == 2 and st["plain_launches"] == 1
