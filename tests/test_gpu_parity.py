@@ -149,6 +149,43 @@ def test_ragged_shapes_full(shape, split, dtype, path):
     assert_bitexact(to_host(ko, dtype), want_k, dtype, "k")
 
 
+def _random_configs(n, seed):
+    """Seeded random shapes, splits, bases and shard placements: half of the splits are multiples of
+    the fast kernel's vector width, half are any even widths."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dtype = oracle.BF16 if rng.random() < 0.6 else oracle.F32
+        step = (8 if dtype == oracle.BF16 else 4) if rng.random() < 0.5 else 2
+        split = tuple(int(step * rng.integers(1, 48 // step + 1)) for _ in range(3))
+        shape = (int(rng.integers(1, 3)), int(rng.integers(1, 7)), int(rng.integers(1, 7)), int(rng.integers(1, 7)),
+                 int(rng.integers(1, 9)), sum(split))
+        base = float(rng.choice([10000.0, 500.0, 1.0e6, 2.5]))
+        offsets = (0, 0, 0) if rng.random() < 0.5 else tuple(int(x) for x in rng.integers(0, 4, 3))
+        out.append((shape, split, dtype, base, offsets))
+    return out
+
+
+@pytest.mark.parametrize("seed", [101, 202, 303])
+def test_random_configurations(seed):
+    """Sixteen random configurations per seed, each through the gate (auto path) and the plain kernel,
+    element by element against the oracle (shards of a larger grid included)."""
+    for shape, split, dtype, base, offsets in _random_configs(16, seed):
+        log(f"random {shape} {split} {dtype} base {base} offsets {offsets}")
+        q, k = workloads.generate_custom(shape, dtype, seed=seed + sum(shape))
+        grid = tuple(n + o for n, o in zip(shape[1:4], offsets))
+        want_q, want_k = oracle.rope3d_qk(q, k, dtype, split, base, offsets=offsets, grid=grid)
+        dq, dk = to_dev(q, dtype), to_dev(k, dtype)
+        for path in (0, 2):
+            rla.set_option(rla.OPT_PATH, path)
+            qo, ko = rla.forward_pair(dq, dk, split, base, grid=grid,
+                                      offsets=None if offsets == (0, 0, 0) else offsets)
+            torch.cuda.synchronize()
+            assert_bitexact(to_host(qo, dtype), want_q, dtype, f"q {shape} {split} path {path}")
+            assert_bitexact(to_host(ko, dtype), want_k, dtype, f"k {shape} {split} path {path}")
+    assert rla.stats()["gate_disabled"] == 0
+
+
 def test_misaligned_views_use_plain_kernel():
     shape, split = (1, 3, 4, 5, 4, 32), (8, 8, 16)
     q, k = workloads.generate_custom(shape, oracle.BF16, seed=5)

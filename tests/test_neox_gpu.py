@@ -164,3 +164,26 @@ def test_precheck_refusals_on_device():
     with pytest.raises(rla.Ltx3dRopeUnsupported):
         rla.neox_apply_qk(dq[:, :, :15].contiguous(), dk[:, :, :15].contiguous(), dpos, dcache[:, :15].contiguous())
     assert rla.stats()["fast_launches"] == 0 and rla.stats()["plain_launches"] == 0
+
+
+@pytest.mark.parametrize("seed", [11, 22])
+def test_random_configurations(seed):
+    """Twenty seeded random configurations per seed (head_dim, head counts, dtypes, cache sizes; half
+    of the head dims give whole 16-byte half rows), fast and plain kernels, against the oracle."""
+    rng = np.random.default_rng(seed)
+    for i in range(20):
+        dtype = oracle.BF16 if rng.random() < 0.6 else oracle.F32
+        cdt = oracle.BF16 if rng.random() < 0.5 else oracle.F32
+        es = 2 if dtype == oracle.BF16 else 4
+        unit = 2 * (16 // es) if rng.random() < 0.5 else 2  # whole 16-byte half rows, or any even D
+        D = int(unit * rng.integers(1, 256 // unit + 1))
+        w = workloads.NeoxWorkload("r", dtype, int(rng.integers(1, 300)), int(rng.integers(1, 21)),
+                                   int(rng.integers(1, 13)), D, int(rng.integers(1, 600)), cdt, "random",
+                                   seed * 100 + i)
+        log(f"random {w}")
+        inputs = workloads.generate_neox(w)
+        for path in (0, 2):
+            (q, k, pos, cache), gq, gk = run(w, path, *inputs)
+            assert_bitexact(gq, nx.neox_rope(q, dtype, pos, cache, cdt), dtype, f"q {w} path {path}")
+            assert_bitexact(gk, nx.neox_rope(k, dtype, pos, cache, cdt), dtype, f"k {w} path {path}")
+    assert rla.neox_position_errors(0) == 0
