@@ -19,13 +19,14 @@
 //    reference path of the bit-exact gate and the fallback for shapes the fast
 //    kernel does not cover.  With VERIFY it recomputes the result and counts
 //    pairs that differ from what the outputs already hold.
-//  * rope_fast: a one-shot grid in which each thread owns one 16-byte vector of
-//    Q and the same vector of K (8 bf16 or 4 fp32 values, i.e. 4 or 2 pairs).
-//    When a token's heads*head_dim row is a whole number of wavefronts, the
-//    token -> (t, h, w) decode runs once per wavefront on scalar values.  The
-//    (cos, sin) row segment of the vector comes from the packed tables with
-//    16-byte loads that stay in the L1/L2 caches (the tables are tens of KB);
-//    Q and K stream through with non-temporal 16-byte loads and stores; bf16
+//  * rope_fast: a one-shot grid in which each thread owns one 16-byte vector
+//    (8 bf16 or 4 fp32 values, i.e. 4 or 2 pairs): the first half of the grid
+//    covers Q, the second half K.  When a token's heads*head_dim row is a whole
+//    number of wavefronts, the token -> (t, h, w) decode runs once per
+//    wavefront on scalar values.  The (cos, sin) row segment of the vector
+//    comes from the packed tables with 16-byte loads that stay in the L1/L2
+//    caches (the tables are tens of KB); Q and K stream through with
+//    non-temporal 16-byte loads and streaming (sc1 | nt) 16-byte stores; bf16
 //    results are packed with the hardware's round-to-nearest-even conversion
 //    (v_cvt_pk_bf16_f32).  Measured on MI355X, this shape streams faster than
 //    a persistent grid with LDS-staged tables and several vectors per lane.
