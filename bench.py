@@ -37,17 +37,21 @@ sys.path.insert(0, ROOT)
 METRIC = "fused Q+K 3D RoPE achieved HBM GB/s (% of peak) + Gelem/s, bit-exact vs oracle"
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rope_fast.json")
-KERNEL_SOURCE = os.path.join(ROOT, "rope_ltx3drope_amd", "csrc", "kernels.hip")
+# the fast kernel's source: its file and the local headers it includes
+KERNEL_SOURCES = [os.path.join(ROOT, "rope_ltx3drope_amd", "csrc", f)
+                  for f in ("kernels.hip", "stream_store.h", "internal.h")]
 
 
 def kernel_source_hash() -> str:
-    """Hash of the fast kernel's source with comments and blank lines removed, so that a change of
-    comments alone does not invalidate the committed counter measurements."""
-    with open(KERNEL_SOURCE, encoding="utf-8") as f:
-        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
-    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
-    code = "\n".join(line for line in lines if line)
-    return hashlib.sha256(code.encode()).hexdigest()[:16]
+    """Hash of the fast kernel's source files with comments and blank lines removed, so that a
+    change of comments alone does not invalidate the committed counter measurements."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+        h.update(("\n".join(line for line in lines if line) + "\n").encode())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload_name: str):
