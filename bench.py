@@ -20,6 +20,8 @@ same unit.
 
 --op neox | patchify | unpatchify time the secondary kernels the same way
 (200 warm-up and 200 timed launches of about 0.13 ms each by default).
+--op dit_freqs times the host-built DiT frequency grid delivered to the device
+(no kernel: float64 host math, one upload; roofline null).
 """
 from __future__ import annotations
 
@@ -79,7 +81,7 @@ def parse():
     ap.add_argument("--grid", type=int, default=0, help="grid index inside the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--op", choices=("rope3d", "neox", "patchify", "unpatchify"), default="rope3d",
+    ap.add_argument("--op", choices=("rope3d", "neox", "patchify", "unpatchify", "dit_freqs"), default="rope3d",
                     help="rope3d: the fused 3D RoPE (default); neox: the rotate-half RoPE with a gathered cache; "
                          "patchify / unpatchify: the stage-5 space-to-depth and its inverse")
     ap.add_argument("--patch-workload", default="p6")
@@ -109,6 +111,8 @@ def main():
         return main_neox(args)
     if args.op in ("patchify", "unpatchify"):
         return main_patch(args)
+    if args.op == "dit_freqs":
+        return main_dit(args)
 
     import numpy as np
     import torch
@@ -344,6 +348,54 @@ def main_neox(args):
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    if mism:
+        sys.exit(1)
+
+
+def main_dit(args):
+    """LTX DiT RoPE frequency grid (theta 10000, dim 4096, 6 rope elements: 682 values) built on the
+    host and delivered to the device, float64 and float32 recipes: time per call (each call ends
+    with the copy to the device complete), bit-exact against the oracle."""
+    import numpy as np
+    import torch
+
+    import oracle.dit_freqs as df
+    import rope_ltx3drope_amd as rla
+
+    dev = torch.device("cuda:0")
+    theta, dim, ne = 10000.0, 4096, 6
+    per_call, mism = {}, 0
+    for double in (True, False):
+        for _ in range(args.warmup):
+            rla.dit_freq_grid(theta, dim, ne, double, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            out = rla.dit_freq_grid(theta, dim, ne, double, device=dev)
+        per_call["f64" if double else "f32"] = (time.perf_counter() - t0) / args.steps
+        want = df.freq_grid(theta, dim, ne, double)
+        mism += int((out.cpu().numpy().view(np.uint32) != want.view(np.uint32)).sum())
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < 1.0:
+        df.freq_grid(theta, dim, ne, True)
+        reps += 1
+    oracle_us = (time.perf_counter() - t0) / reps * 1e6
+    us = per_call["f64"] * 1e6
+    line = {
+        "metric": "LTX DiT RoPE frequency grid delivered to the device, time per call, bit-exact vs oracle",
+        "value": round(us, 2), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic (fixed parameters)",
+        "config": {"workload": "dit_freqs_theta1e4_dim4096_ne6", "values": dim // ne,
+                   "f32_recipe_us": round(per_call["f32"] * 1e6, 2)},
+        "kernel": None, "parity": {"compared_elements": 2 * (dim // ne), "mismatching_elements": mism,
+                                   "tolerance_ulp": 0},
+        "roofline": None,
+        "cpu_baseline": {"value": round(oracle_us, 2), "unit": "us", "cores": 1, "kind": "oracle",
+                         "sample": "the float64 recipe, host array only"},
     }
     print(json.dumps(line), flush=True)
     if mism:
