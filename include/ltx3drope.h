@@ -27,8 +27,9 @@
  * multiply-add ("Key source snippets", the kernel's pair-rotation helper):
  *     e' = (e*c) - (o*s),   o' = (e*s) + (o*c)
  * then cast back to the tensor dtype (bf16: round to nearest, ties to even;
- * fp32: identity).  Q and K use the same (c, s).  Results are written out of
- * place; inputs are never modified.
+ * fp32: identity).  Q and K use the same (c, s).  ltx3drope_apply_qk writes
+ * out of place and never modifies its inputs; the shard entry point can also
+ * rotate in place (see ltx3drope_shard_t).
  *
  * All functions are thread-safe, never throw, and return a status code
  * (LTX3DROPE_OK == 0, negative on error) unless stated otherwise.  Pointers
@@ -153,8 +154,9 @@ int ltx3drope_cache_clear(void);
  *
  * Returns 1 if ltx3drope_apply_qk would launch for these arguments, 0 if it
  * would refuse.  q_out and k_out may both be NULL: then only the inputs are
- * checked (for a caller that allocates fresh outputs afterwards); when `reason` is not NULL it receives an LTX3DROPE_REASON_*
- * code (the first failing rule in the order of the enum).  Rules: no NULL
+ * checked (for a caller that allocates fresh outputs afterwards).  When
+ * `reason` is not NULL it receives an LTX3DROPE_REASON_* code (the first
+ * failing rule in the order of the enum).  Rules: no NULL
  * pointer or handle; dtype F32 or BF16; B, T, H, W, heads, head_dim > 0;
  * table split widths even and > 0 and summing to head_dim; tables built for
  * (T, H, W); every pointer aligned to one pair (8 B for F32, 4 B for BF16);
