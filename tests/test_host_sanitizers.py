@@ -1,0 +1,43 @@
+"""The library's host code under AddressSanitizer + UndefinedBehaviorSanitizer and under
+ThreadSanitizer (CPU only).
+
+api.cpp and tables.cpp are compiled for the host with clang and the sanitizer, linked with
+stand-ins for the HIP runtime and the kernel launchers (tests/host_sanitize/stubs.cpp), and
+driven by tests/host_sanitize/driver.cpp: eight threads build, read, hold and release table
+sets of 24 grids through the 16-entry cache (evictions while handles are held), run the
+precheck, refused launches, statistics, cache clears and the DiT frequency grid, all in
+host-table mode.  At the end every table must be freed and no HIP stand-in called.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CLANG = "/opt/rocm/llvm/bin/clang++"
+SOURCES = [os.path.join(ROOT, "rope_ltx3drope_amd", "csrc", "api.cpp"),
+           os.path.join(ROOT, "rope_ltx3drope_amd", "csrc", "tables.cpp"),
+           os.path.join(ROOT, "tests", "host_sanitize", "stubs.cpp"),
+           os.path.join(ROOT, "tests", "host_sanitize", "driver.cpp")]
+
+pytestmark = pytest.mark.skipif(not shutil.which(CLANG), reason="clang++ of the ROCm toolchain not found")
+
+
+@pytest.mark.parametrize("sanitizer,iters", [("address,undefined", 2000), ("thread", 1000)],
+                         ids=["asan_ubsan", "tsan"])
+def test_host_code_under_sanitizer(tmp_path, sanitizer, iters):
+    exe = tmp_path / "driver"
+    cmd = [CLANG, "-x", "c++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           f"-fsanitize={sanitizer}", "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"),
+           "-I" + os.path.join(ROOT, "rope_ltx3drope_amd", "csrc"), *SOURCES, "-o", str(exe), "-lpthread"]
+    build = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert build.returncode == 0, build.stderr[-3000:]
+    run = subprocess.run([str(exe), "8", str(iters)], capture_output=True, text=True, timeout=300)
+    out = run.stdout + run.stderr
+    assert run.returncode == 0, out[-4000:]
+    assert "Sanitizer" not in out and "runtime error" not in out, out[-4000:]
+    assert "host sanitizer driver" in run.stdout
