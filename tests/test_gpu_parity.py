@@ -280,6 +280,25 @@ def test_workload4_outliers():
     fast_equals_plain(dq, dk, qo, ko, w.split, w.base)
 
 
+def test_fp32_at_workload4_size():
+    """The fp32 fast kernel (two pairs per vector) at full size: workload 4's geometry in fp32
+    (1.8 GB per tensor), sampled tokens against the oracle and fast == plain over the whole output."""
+    shape, split = (1, 16, 96, 96, 24, 128), (32, 48, 48)
+    log("fp32 at workload 4 size: generating inputs")
+    q, k = workloads.generate_custom(shape, oracle.F32, seed=44)
+    dq, dk = to_dev(q, oracle.F32), to_dev(k, oracle.F32)
+    qo, ko = run(dq, dk, split)
+    assert rla.stats()["fast_launches"] >= 1 and rla.stats()["gate_disabled"] == 0
+    B, T, H, W, heads, D = shape
+    for x, out, seed in ((q, qo, 42), (k, ko, 43)):
+        ids = workloads.sample_tokens(B * T * H * W, 2000, seed)
+        want = oracle.rope3d_sampled(x, oracle.F32, split, ids)
+        got = to_host(out.view(B * T * H * W, heads, D)[torch.from_numpy(ids).to(DEV)], oracle.F32)
+        assert_bitexact(got, want, oracle.F32, "fp32 workload-4 geometry, sampled tokens")
+    del q, k
+    fast_equals_plain(dq, dk, qo, ko, split, 10000.0)
+
+
 def test_workload5_three_alternating_grids():
     w = workloads.WORKLOADS[5]
     log("workload 5: generating inputs for three grids")
