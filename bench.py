@@ -26,6 +26,7 @@ same unit.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import re
 import json
@@ -86,6 +87,8 @@ def parse():
                          "patchify / unpatchify: the stage-5 space-to-depth and its inverse")
     ap.add_argument("--patch-workload", default="p6")
     ap.add_argument("--neox-workload", default="n4")
+    ap.add_argument("--dtype", choices=("auto", "f32", "bf16"), default="auto",
+                    help="rope3d: run the workload's geometry in this dtype (auto: the workload's own)")
     ap.add_argument("--graph", action="store_true",
                     help="rope3d: capture the K timed launches in one HIP graph and time its replay "
                          "(for the launch-bound small workloads); the default is eager launches")
@@ -125,6 +128,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     w = workloads.WORKLOADS[args.workload]
+    if args.dtype not in ("auto", w.dtype):
+        # the same geometry, split, base, seed and value recipe in the other dtype
+        w = dataclasses.replace(w, dtype=args.dtype, name=f"{w.name}_as_{args.dtype}")
     gi = args.grid
     B, T, H, W, heads, D = w.shape(gi)
     numel = w.numel(gi)
