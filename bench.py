@@ -89,6 +89,8 @@ def parse():
     ap.add_argument("--neox-workload", default="n4")
     ap.add_argument("--dtype", choices=("auto", "f32", "bf16"), default="auto",
                     help="rope3d: run the workload's geometry in this dtype (auto: the workload's own)")
+    ap.add_argument("--split", default="",
+                    help="rope3d: dim_t,dim_h,dim_w instead of the workload's split (same head_dim)")
     ap.add_argument("--graph", action="store_true",
                     help="rope3d: capture the K timed launches in one HIP graph and time its replay "
                          "(for the launch-bound small workloads); the default is eager launches")
@@ -131,6 +133,11 @@ def main():
     if args.dtype not in ("auto", w.dtype):
         # the same geometry, split, base, seed and value recipe in the other dtype
         w = dataclasses.replace(w, dtype=args.dtype, name=f"{w.name}_as_{args.dtype}")
+    if args.split:
+        split = tuple(int(x) for x in args.split.split(","))
+        if len(split) != 3 or sum(split) != w.head_dim:
+            raise SystemExit(f"--split needs three even widths summing to head_dim {w.head_dim}")
+        w = dataclasses.replace(w, split=split, name=f"{w.name}_split{'_'.join(map(str, split))}")
     gi = args.grid
     B, T, H, W, heads, D = w.shape(gi)
     numel = w.numel(gi)

@@ -185,14 +185,19 @@ struct FastArgs {
     uint32_t V;        // 16-B vectors per head
     uint32_t N, HW, W;
     uint32_t PT, PH;   // pairs in the t and h chunks
-    uint32_t rowT4, rowH4, rowW4;  // float4 per table row of each section
-    uint32_t offH4, offW4;         // first float4 of the h and w sections
+    uint32_t rowT4, rowH4, rowW4;  // float4 per table row of each section (ALIGNED)
+    uint32_t offH4, offW4;         // first float4 of the h and w sections (ALIGNED)
+    uint32_t PW;                   // pairs in the w chunk
+    uint32_t offH2, offW2;         // first (cos, sin) pair of the h and w sections
     uint32_t t_off, h_off, w_off;  // global coordinate of the tensor's first frame / row / column
 };
 
-// PPV pairs per 16-B vector: 4 for bf16, 2 for fp32.  Every chunk width is a
-// multiple of PPV pairs (checked on the host), so a vector never straddles two
-// chunks and its PPV (cos, sin) pairs are PPV/2 consecutive float4 of one row.
+// PPV pairs per 16-B vector: 4 for bf16, 2 for fp32.  ALIGNED: the t and h chunk
+// widths are multiples of PPV pairs (so is the w chunk, as head_dim is a whole
+// number of vectors), so a vector never straddles two chunks and its PPV
+// (cos, sin) pairs are PPV/2 consecutive float4 of one row.  Otherwise (any even
+// split) each pair finds its chunk and row on its own and loads its (cos, sin)
+// as one float2.
 //
 // Grid: 2 * ceil(vectors / 64) workgroups of one wavefront.  The first half of
 // the grid rotates Q, the second half K, so that while the grid runs the memory
@@ -210,7 +215,7 @@ struct FastArgs {
 // streaming store (sc1 | nt): every byte is touched exactly once, so the streams
 // should not displace other data from the caches (measured: +3 to +10 % on the
 // 0.8-6.8 GB workloads for the hints, about +1 % more for the store policy).
-template <bool BF16, bool WAVE_TOKEN>
+template <bool BF16, bool WAVE_TOKEN, bool ALIGNED>
 __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
     constexpr uint32_t PPV = BF16 ? 4 : 2;
     const uint32_t half = gridDim.x >> 1;
@@ -238,21 +243,45 @@ __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
     const uint32_t h = hl + a.h_off;
     const uint32_t w = rem - hl * a.W + a.w_off;
     const uint32_t j0 = (u % a.V) * PPV;  // first pair of this vector inside its head
-    uint32_t idx;
-    if (j0 < a.PT) {
-        idx = t * a.rowT4 + j0 / 2;
-    } else if (j0 < a.PT + a.PH) {
-        idx = a.offH4 + h * a.rowH4 + (j0 - a.PT) / 2;
-    } else {
-        idx = a.offW4 + w * a.rowW4 + (j0 - a.PT - a.PH) / 2;
-    }
     const u32x4 x = __builtin_nontemporal_load(src + g);
-    const f32x4 cs0 = a.tab[idx];  // (c0, s0, c1, s1)
+    float c[PPV], s[PPV];
+    if constexpr (ALIGNED) {
+        uint32_t idx;
+        if (j0 < a.PT) {
+            idx = t * a.rowT4 + j0 / 2;
+        } else if (j0 < a.PT + a.PH) {
+            idx = a.offH4 + h * a.rowH4 + (j0 - a.PT) / 2;
+        } else {
+            idx = a.offW4 + w * a.rowW4 + (j0 - a.PT - a.PH) / 2;
+        }
+#pragma unroll
+        for (uint32_t r = 0; r < PPV / 2; ++r) {
+            const f32x4 cs = a.tab[idx + r];  // (c, s) of two consecutive pairs
+            c[2 * r] = cs.x;
+            s[2 * r] = cs.y;
+            c[2 * r + 1] = cs.z;
+            s[2 * r + 1] = cs.w;
+        }
+    } else {
+        const f32x2* tab2 = reinterpret_cast<const f32x2*>(a.tab);
+#pragma unroll
+        for (uint32_t r = 0; r < PPV; ++r) {
+            const uint32_t j = j0 + r;
+            uint32_t idx;
+            if (j < a.PT) {
+                idx = t * a.PT + j;
+            } else if (j < a.PT + a.PH) {
+                idx = a.offH2 + h * a.PH + (j - a.PT);
+            } else {
+                idx = a.offW2 + w * a.PW + (j - a.PT - a.PH);
+            }
+            const f32x2 cs = tab2[idx];
+            c[r] = cs.x;
+            s[r] = cs.y;
+        }
+    }
     u32x4 y;
     if constexpr (BF16) {
-        const f32x4 cs1 = a.tab[idx + 1];  // (c2, s2, c3, s3)
-        const float c[4] = {cs0.x, cs0.z, cs1.x, cs1.z};
-        const float s[4] = {cs0.y, cs0.w, cs1.y, cs1.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float ye, yo;
@@ -261,8 +290,8 @@ __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
         }
     } else {
         float y0, y1, y2, y3;
-        rotate(__uint_as_float(x.x), __uint_as_float(x.y), cs0.x, cs0.y, y0, y1);
-        rotate(__uint_as_float(x.z), __uint_as_float(x.w), cs0.z, cs0.w, y2, y3);
+        rotate(__uint_as_float(x.x), __uint_as_float(x.y), c[0], s[0], y0, y1);
+        rotate(__uint_as_float(x.z), __uint_as_float(x.w), c[1], s[1], y2, y3);
         y = (u32x4){__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
     }
     stream_store16(y, dst + blk * kFastBlock, kFastBlock * 16u, threadIdx.x * 16u);
@@ -349,12 +378,23 @@ hipError_t launch_plain_impl(const Problem& p, unsigned* mismatches, hipStream_t
 
 bool fast_supported(const Problem& p) {
     const uint32_t es = elem_size(p);
-    const uint32_t ppv = 8u / es;  // pairs per 16-B vector
     for (const void* ptr : {static_cast<const void*>(p.q), static_cast<const void*>(p.k),
                             static_cast<const void*>(p.q_out), static_cast<const void*>(p.k_out)})
         if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return false;
-    if ((p.D * es) % 16 != 0) return false;
-    return p.PT % ppv == 0 && p.PH % ppv == 0 && p.PW % ppv == 0;
+    return (p.D * es) % 16 == 0;  // head rows are whole 16-byte vectors; any even split
+}
+
+template <bool ALIGNED>
+hipError_t launch_fast_split(const FastArgs& a, bool bf16, bool wave_token, uint32_t blocks, hipStream_t stream) {
+    if (bf16 && wave_token)
+        hipLaunchKernelGGL((rope_fast<true, true, ALIGNED>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    else if (bf16)
+        hipLaunchKernelGGL((rope_fast<true, false, ALIGNED>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    else if (wave_token)
+        hipLaunchKernelGGL((rope_fast<false, true, ALIGNED>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    else
+        hipLaunchKernelGGL((rope_fast<false, false, ALIGNED>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
@@ -382,21 +422,19 @@ hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
     a.t_off = p.t_off;
     a.h_off = p.h_off;
     a.w_off = p.w_off;
+    a.PW = p.PW;
+    a.offH2 = p.tabT * p.PT;
+    a.offW2 = p.tabT * p.PT + p.tabH * p.PH;
     const uint32_t per_tensor = (a.total + kFastBlock - 1) / kFastBlock;
     if (per_tensor == 0) return hipSuccess;
     const uint32_t blocks = 2 * per_tensor;  // first half Q, second half K
     const bool wave_token = a.HV % 64 == 0;
     const bool bf16 = p.dtype == LTX3DROPE_DTYPE_BF16;
+    const uint32_t ppv = 8u / es;
+    const bool aligned = p.PT % ppv == 0 && p.PH % ppv == 0;
     (void)device;
-    if (bf16 && wave_token)
-        hipLaunchKernelGGL((rope_fast<true, true>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    else if (bf16)
-        hipLaunchKernelGGL((rope_fast<true, false>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    else if (wave_token)
-        hipLaunchKernelGGL((rope_fast<false, true>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    else
-        hipLaunchKernelGGL((rope_fast<false, false>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    return hipGetLastError();
+    if (aligned) return launch_fast_split<true>(a, bf16, wave_token, blocks, stream);
+    return launch_fast_split<false>(a, bf16, wave_token, blocks, stream);
 }
 
 hipError_t launch_plain(const Problem& p, hipStream_t stream, int device) {

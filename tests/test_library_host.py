@@ -344,11 +344,12 @@ def test_kernel_choice_rules():
         # head rows that are not a whole number of 16-byte vectors -> plain
         with rla.tables_build(2, 3, 4, (8, 8, 4)) as tab2:
             assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_BF16, 1, 2, 3, 4, 3, 20, tab2.handle) == 2
-    with rla.tables_build(2, 3, 4, (2, 6, 4)) as tab:  # chunk widths not multiples of 4 pairs
+    with rla.tables_build(2, 3, 4, (2, 6, 4)) as tab:  # bf16 head row of 24 bytes: not whole vectors
         assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_BF16, 1, 2, 3, 4, 2, 12, tab.handle) == 2
-    with rla.tables_build(2, 3, 4, (4, 8, 4)) as tab:  # fp32: 2 pairs per vector
+        assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_F32, 1, 2, 3, 4, 2, 12, tab.handle) == 1
+    with rla.tables_build(2, 3, 4, (4, 8, 4)) as tab:  # chunk widths not multiples of a vector's pairs
         assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_F32, 1, 2, 3, 4, 2, 16, tab.handle) == 1
-        assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_BF16, 1, 2, 3, 4, 2, 16, tab.handle) == 2
+        assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_BF16, 1, 2, 3, 4, 2, 16, tab.handle) == 1
 
 
 # ---------------------------------------------------------------------------
