@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rope_fast.json")
 # the fast kernel's source: its file and the local headers it includes
 KERNEL_SOURCES = [os.path.join(ROOT, "rope_ltx3drope_amd", "csrc", f)
-                  for f in ("kernels.hip", "stream_store.h", "internal.h")]
+                  for f in ("kernels.hip", "stream_store.h", "internal.h", "fastdiv.h")]
 
 
 def kernel_source_hash() -> str:

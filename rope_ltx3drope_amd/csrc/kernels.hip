@@ -35,6 +35,7 @@
 #include <map>
 #include <mutex>
 
+#include "fastdiv.h"
 #include "internal.h"
 #include "stream_store.h"
 
@@ -190,6 +191,7 @@ struct FastArgs {
     uint32_t PW;                   // pairs in the w chunk
     uint32_t offH2, offW2;         // first (cos, sin) pair of the h and w sections
     uint32_t t_off, h_off, w_off;  // global coordinate of the tensor's first frame / row / column
+    FastDiv div_HV, div_V, div_N, div_HW, div_W;  // the token decode's divisors (fastdiv.h)
 };
 
 // PPV pairs per 16-B vector: 4 for bf16, 2 for fp32.  ALIGNED: the t and h chunk
@@ -228,21 +230,21 @@ __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
     if constexpr (WAVE_TOKEN) {
         const uint32_t g0 = blk * kFastBlock;
         if (g0 >= a.total) return;  // whole wavefronts: total is a multiple of 64 here
-        tok = g0 / a.HV;
+        tok = fast_div(g0, a.div_HV);
         u = (g0 - tok * a.HV) + threadIdx.x;
     } else {
         if (g >= a.total) return;
-        tok = g / a.HV;
+        tok = fast_div(g, a.div_HV);
         u = g - tok * a.HV;
     }
-    const uint32_t n = tok % a.N;
-    const uint32_t tl = n / a.HW;  // local coordinates, then global ones
+    const uint32_t n = fast_mod(tok, a.div_N);
+    const uint32_t tl = fast_div(n, a.div_HW);  // local coordinates, then global ones
     const uint32_t rem = n - tl * a.HW;
-    const uint32_t hl = rem / a.W;
+    const uint32_t hl = fast_div(rem, a.div_W);
     const uint32_t t = tl + a.t_off;
     const uint32_t h = hl + a.h_off;
     const uint32_t w = rem - hl * a.W + a.w_off;
-    const uint32_t j0 = (u % a.V) * PPV;  // first pair of this vector inside its head
+    const uint32_t j0 = fast_mod(u, a.div_V) * PPV;  // first pair of this vector inside its head
     const u32x4 x = __builtin_nontemporal_load(src + g);
     float c[PPV], s[PPV];
     if constexpr (ALIGNED) {
@@ -422,6 +424,11 @@ hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
     a.t_off = p.t_off;
     a.h_off = p.h_off;
     a.w_off = p.w_off;
+    a.div_HV = make_fastdiv(a.HV);
+    a.div_V = make_fastdiv(a.V);
+    a.div_N = make_fastdiv(a.N);
+    a.div_HW = make_fastdiv(a.HW);
+    a.div_W = make_fastdiv(a.W);
     a.PW = p.PW;
     a.offH2 = p.tabT * p.PT;
     a.offW2 = p.tabT * p.PT + p.tabH * p.PH;

@@ -41,3 +41,17 @@ def test_host_code_under_sanitizer(tmp_path, sanitizer, iters):
     assert run.returncode == 0, out[-4000:]
     assert "Sanitizer" not in out and "runtime error" not in out, out[-4000:]
     assert "host sanitizer driver" in run.stdout
+
+
+def test_fast_division_matches_hardware_division(tmp_path):
+    """fastdiv.h (the kernels' division by invariant divisors) against the hardware division:
+    sampled dividends for every divisor up to 2^16 and 200000 random ones, every dividend for two."""
+    gxx = shutil.which("g++") or CLANG
+    exe = tmp_path / "fastdiv_check"
+    src = os.path.join(ROOT, "tests", "host_sanitize", "fastdiv_check.cpp")
+    build = subprocess.run([gxx, "-O2", "-std=c++17", "-I" + os.path.join(ROOT, "rope_ltx3drope_amd", "csrc"), src,
+                            "-o", str(exe)], capture_output=True, text=True, timeout=300)
+    assert build.returncode == 0, build.stderr[-3000:]
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "0 differ" in run.stdout
