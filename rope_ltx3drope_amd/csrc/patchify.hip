@@ -34,6 +34,7 @@
 // streaming (sc1 | nt) stores.
 #include <hip/hip_runtime.h>
 
+#include "fastdiv.h"
 #include "internal.h"
 #include "stream_store.h"
 
@@ -57,6 +58,7 @@ struct PatchArgs {
     uint32_t groups;          // patch_fast: B*C*F*H*groups_per_row; LDS kernels: 16-byte vectors of the unpatched tensor
     uint64_t numel;           // plain kernel
     uint32_t dst_bytes;       // LDS kernels: output size in bytes when below 2^31 (streaming stores), else 0
+    FastDiv div_WE, div_WpE, div_Hp, div_F;  // LDS kernels: W/E, (W/p)/E, H/p and F (fastdiv.h)
 };
 
 // LDS kernels' 16-byte store at element offset `off` of the output: a streaming store (sc1 | nt)
@@ -140,24 +142,23 @@ struct RowId {
 };
 
 template <int P>
-__device__ __forceinline__ RowId decode_row(uint32_t rowid, uint32_t Hp, uint32_t F) {
+__device__ __forceinline__ RowId decode_row(uint32_t rowid, const PatchArgs& a) {
     RowId d;
-    d.hh = rowid % Hp;
-    const uint32_t t = rowid / Hp;
+    const uint32_t t = fast_div(rowid, a.div_Hp);
+    d.hh = rowid - t * a.div_Hp.d;
     d.ph = t % P;
     const uint32_t bcf = t / P;
-    d.bc = bcf / F;
-    d.f = bcf - d.bc * F;
+    d.bc = fast_div(bcf, a.div_F);
+    d.f = bcf - d.bc * a.F;
     return d;
 }
 
 // Element offset of unpatched vector I (16-byte vectors in (b, c, f, ph, hh, x) order).
 template <int P, int E>
 __device__ __forceinline__ uint64_t unpatched_offset(const PatchArgs& a, uint32_t I) {
-    const uint32_t WE = a.W / E;
-    const uint32_t rowid = I / WE;
-    const uint32_t x = I - rowid * WE;
-    const RowId d = decode_row<P>(rowid, a.H / P, a.F);
+    const uint32_t rowid = fast_div(I, a.div_WE);
+    const uint32_t x = I - rowid * a.div_WE.d;
+    const RowId d = decode_row<P>(rowid, a);
     const uint64_t row = (static_cast<uint64_t>(d.bc) * a.F + d.f) * a.H + d.hh * P + d.ph;
     return row * a.W + static_cast<uint64_t>(x) * E;
 }
@@ -167,10 +168,9 @@ __device__ __forceinline__ uint64_t unpatched_offset(const PatchArgs& a, uint32_
 template <int P, int E>
 __device__ __forceinline__ uint64_t packed_offset0(const PatchArgs& a, uint32_t O) {
     const uint32_t Hp = a.H / P, Wp = a.W / P;
-    const uint32_t WpE = Wp / E;
-    const uint32_t rowid = O / WpE;
-    const uint32_t wv = O - rowid * WpE;
-    const RowId d = decode_row<P>(rowid, Hp, a.F);
+    const uint32_t rowid = fast_div(O, a.div_WpE);
+    const uint32_t wv = O - rowid * a.div_WpE.d;
+    const RowId d = decode_row<P>(rowid, a);
     const uint64_t co = static_cast<uint64_t>(d.bc) * P * P + d.ph;  // output channel of width offset 0
     return ((co * a.F + d.f) * Hp + d.hh) * Wp + static_cast<uint64_t>(wv) * E;
 }
@@ -356,7 +356,7 @@ bool patch_fast_supported(const PatchProblem& p) {
 }
 
 hipError_t launch_patch(const PatchProblem& p, bool inverse, hipStream_t stream, int cu_count) {
-    PatchArgs a;
+    PatchArgs a{};
     a.src = p.src;
     a.dst = p.dst;
     a.B = p.B;
@@ -375,6 +375,10 @@ hipError_t launch_patch(const PatchProblem& p, bool inverse, hipStream_t stream,
         const uint32_t E = 16 / p.elem_bytes;
         if (E % p.p == 0) {
             a.groups = static_cast<uint32_t>(a.numel / E);  // 16-byte vectors of the unpatched tensor
+            a.div_WE = make_fastdiv(p.W / E);
+            a.div_WpE = make_fastdiv(p.W / p.p / E);
+            a.div_Hp = make_fastdiv(p.H / p.p);
+            a.div_F = make_fastdiv(p.F);
             const uint32_t blocks = (a.groups + p.p * kBlock - 1) / (p.p * kBlock);
             return p.elem_bytes == 2 ? launch_lds_t<uint16_t>(a, p.p, inverse, blocks, stream)
                                      : launch_lds_t<uint32_t>(a, p.p, inverse, blocks, stream);
