@@ -94,6 +94,8 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="rope3d: capture the K timed launches in one HIP graph and time its replay "
                          "(for the launch-bound small workloads); the default is eager launches")
+    ap.add_argument("--reuse-outputs", action="store_true",
+                    help="rope3d: write into output buffers allocated once per input set instead of fresh ones")
     ap.add_argument("--inplace", action="store_true",
                     help="rope3d: rotate Q and K in place instead of into fresh outputs")
     ap.add_argument("--rotate", type=int, default=0,
@@ -165,6 +167,8 @@ def main():
     sets = [(q, k)] + [(q.clone(), k.clone()) for _ in range(rotate - 1)]
     counter = [0]
     applied = [0] * rotate  # in-place mode: rotations applied to each input set so far
+    # --reuse-outputs: one output pair per input set, allocated once (a serving loop's buffers)
+    reused = [(torch.empty_like(q), torch.empty_like(k)) for _ in range(rotate)] if args.reuse_outputs else []
 
     def step():
         qi, ki = sets[counter[0] % rotate]
@@ -175,8 +179,11 @@ def main():
             rla.apply_qk(qi, ki, tab, inplace=True)
             tab.close()
             return qi, ki
-        qo = torch.empty_like(qi)
-        ko = torch.empty_like(ki)
+        if args.reuse_outputs:
+            qo, ko = reused[(counter[0] - 1) % rotate]
+        else:
+            qo = torch.empty_like(qi)
+            ko = torch.empty_like(ki)
         rla.apply_qk(qi, ki, tab, qo, ko)
         tab.close()
         return qo, ko
@@ -304,7 +311,7 @@ def main():
                    "rope_dim_split": list(w.split), "base": w.base, "tokens": B * T * H * W,
                    "algorithmic_bytes_per_step": alg_bytes, "input_sets": rotate, "parallelism": "single GPU",
                    "launch": "hip_graph" if args.graph else "eager",
-                   "outputs": "in_place" if args.inplace else "fresh"},
+                   "outputs": "in_place" if args.inplace else ("reused" if args.reuse_outputs else "fresh")},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "gelem_per_s": round(elems / (wall / args.steps) / 1e9, 2),
         "kernel": kernel,
