@@ -77,10 +77,18 @@ def _dtype_code(t) -> int:
 
 
 def _stream_ptr(device, stream=None) -> int:
+    """The hipStream_t of `stream`, or of torch's current stream on `device` (a torch device or an
+    index)."""
     torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return int(stream.cuda_stream)
+    if stream is not None:
+        return int(stream.cuda_stream)
+    idx = device if isinstance(device, int) else device.index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)  # the same pointer, without a Stream object
+    if raw is not None:
+        return int(raw(idx))
+    return int(torch.cuda.current_stream(idx).cuda_stream)
 
 
 class Tables:
@@ -144,7 +152,7 @@ def tables_build(T: int, H: int, W: int, split: Sequence[int], base: float = 100
     dt, dh, dw = (int(x) for x in split)
     out = ctypes.c_void_p()
     host_mode = get_option(OPT_HOST_TABLES) != 0
-    sp = 0 if host_mode else _stream_ptr(_torch().device("cuda", device), stream)
+    sp = 0 if host_mode else _stream_ptr(int(device), stream)
     _check(_lib.lib().ltx3drope_tables_build(int(device), int(T), int(H), int(W), dt, dh, dw, float(base), sp,
                                               ctypes.byref(out)), "tables_build")
     return Tables(out.value)
