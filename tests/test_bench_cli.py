@@ -1,0 +1,62 @@
+"""bench.py's command line (CPU): the one-GPU rule, per-op defaults and argument checks."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def parse(*argv):
+    old = sys.argv
+    sys.argv = ["bench.py", *argv]
+    try:
+        return bench.parse()
+    finally:
+        sys.argv = old
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_defaults_per_op():
+    a = parse()
+    assert (a.op, a.workload, a.steps, a.warmup, a.gpus) == ("rope3d", 5, 50, 20, 1)
+    for op in ("neox", "patchify", "unpatchify", "dit_freqs"):
+        a = parse("--op", op)
+        assert (a.steps, a.warmup) == (200, 200)
+    a = parse("--steps", "7", "--warmup", "3")
+    assert (a.steps, a.warmup) == (7, 3)
+
+
+def test_kernel_source_hash_ignores_comments(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("// a comment\nint x = 1;  // trailing\n/* block\ncomment */\nint y = 2;\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src)])
+    h1 = bench.kernel_source_hash()
+    src.write_text("int x = 1;\n\n// other words\nint y = 2;\n")
+    assert bench.kernel_source_hash() == h1
+    src.write_text("int x = 1;\nint y = 3;\n")
+    assert bench.kernel_source_hash() != h1
+
+
+def test_traffic_record_is_used_only_for_the_source_it_was_taken_on():
+    """bench.py reports the committed counter traffic only while the kernel source is the one the
+    counters were taken on (else null)."""
+    import json
+
+    rec = json.load(open(bench.TRAFFIC_FILE))
+    assert 1.0 <= rec["traffic_over_algorithmic"] < 1.01
+    assert bench.measured_traffic("another workload") is None
+    if rec["kernel_source_sha256_16"] == bench.kernel_source_hash():
+        assert bench.measured_traffic(rec["workload"]) == rec["bytes_per_launch"]
+    else:
+        assert bench.measured_traffic(rec["workload"]) is None
