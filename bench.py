@@ -19,7 +19,8 @@ oracle timed on the host on a bounded slab of the same workload, scaled to the
 same unit.
 
 --op neox | patchify | unpatchify time the secondary kernels the same way
-(200 warm-up and 200 timed launches of about 0.13 ms each by default).
+(200 warm-up and 200 timed launches of about 0.13 ms each by default), with
+their own counter records and CPU-oracle baselines.
 --op dit_freqs times the host-built DiT frequency grid delivered to the device
 (no kernel: float64 host math, one upload; roofline null).
 """
@@ -39,35 +40,57 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused Q+K 3D RoPE achieved HBM GB/s (% of peak) + Gelem/s, bit-exact vs oracle"
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rope_fast.json")
-# the fast kernel's source: its file and the local headers it includes
-KERNEL_SOURCES = [os.path.join(ROOT, "rope_ltx3drope_amd", "csrc", f)
-                  for f in ("kernels.hip", "stream_store.h", "internal.h", "fastdiv.h")]
+CSRC = os.path.join(ROOT, "rope_ltx3drope_amd", "csrc")
+# each timed kernel: its source file and the local headers it includes
+KERNEL_SOURCES = {
+    "rope_fast": ("kernels.hip", "stream_store.h", "internal.h", "fastdiv.h"),
+    "neox_fast": ("neox.hip", "stream_store.h", "internal.h"),
+    "patch_lds": ("patchify.hip", "stream_store.h", "internal.h", "fastdiv.h"),
+    "unpatch_lds": ("patchify.hip", "stream_store.h", "internal.h", "fastdiv.h"),
+}
 
 
-def kernel_source_hash() -> str:
-    """Hash of the fast kernel's source files with comments and blank lines removed, so that a
-    change of comments alone does not invalidate the committed counter measurements."""
+def traffic_file(kernel: str) -> str:
+    """The committed rocprofv3 counter record of one kernel."""
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+
+
+TRAFFIC_FILE = traffic_file("rope_fast")
+
+
+def kernel_source_hash(kernel: str = "rope_fast") -> str:
+    """Hash of a kernel's source files with comments and blank lines removed, so that a change of
+    comments alone does not invalidate the committed counter measurements."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, encoding="utf-8") as f:
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
         lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
         h.update(("\n".join(line for line in lines if line) + "\n").encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
-    the kernel source that is built now (otherwise None)."""
+def measured_traffic(workload_name: str, kernel: str = "rope_fast"):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on this
+    workload and on the kernel source that is built now (otherwise None)."""
+    if kernel not in KERNEL_SOURCES:
+        return None
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash() or rec.get("workload") != workload_name:
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(kernel) or rec.get("workload") != workload_name:
         return None
     return rec.get("bytes_per_launch")
+
+
+def pin_one_core():
+    """Run the calling process on one core, so the CPU baseline states the threads it used."""
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
 
 
 def parse():
@@ -385,6 +408,8 @@ def main_neox(args):
         got = got.view(torch.int16).numpy().view(np.uint16) if w.dtype == workloads.BF16 else got.numpy()
         mism += int((got.view(want.dtype) != want).sum())
     st = rla.stats()
+    kernel = "neox_fast" if st["fast_launches"] else "neox_plain"
+    cpu = None if args.no_cpu_baseline else neox_cpu_baseline(w, q_np, k_np, pos_np, cache_np, args.cpu_seconds)
     line = {
         "metric": "rotate-half RoPE with gathered cos/sin cache, achieved HBM GB/s, bit-exact vs oracle",
         "value": round(alg / (wall / args.steps) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -394,12 +419,13 @@ def main_neox(args):
                    "head_dim": w.head_dim, "max_position": w.max_position, "cache_dtype": w.cache_dtype,
                    "positions": w.positions, "algorithmic_bytes_per_step": alg, "input_sets": rotate,
                    "outputs": "reused" if args.reuse_outputs else "fresh"},
-        "kernel": "neox_fast" if st["fast_launches"] else "neox_plain",
+        "kernel": kernel,
         "kernel_avg_us": round(kavg * 1e6, 2),
         "parity": {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0},
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
-        "cpu_baseline": None,
+                     "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.key, kernel)},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     if mism:
@@ -509,28 +535,85 @@ def main_patch(args):
     wall = time.perf_counter() - t0
     kavg = e0.elapsed_time(e1) / args.steps / 1e3  # launches run back to back: no marker between them
     got = outs[-1].cpu().numpy().view(x_np.dtype)
-    want = x_np if inverse else pf.patchify(x_np, p)
+    del outs, sets
+    # the oracle on the whole workload: the parity reference for patchify and, repeated on one core
+    # for about --cpu-seconds, the CPU baseline of either direction
+    if inverse:
+        want = x_np
+        fn_cpu, src_cpu = pf.unpatchify, None if args.no_cpu_baseline else pf.patchify(x_np, p)
+    else:
+        fn_cpu, src_cpu = pf.patchify, x_np
+    cpu, calls, cpu_s = None, 0, 0.0
+    if not args.no_cpu_baseline:
+        pin_one_core()
+    while src_cpu is not None:
+        t0 = time.perf_counter()
+        res = fn_cpu(src_cpu, p)
+        cpu_s += time.perf_counter() - t0
+        calls += 1
+        if not inverse and calls == 1:
+            want = res
+        del res
+        if args.no_cpu_baseline or cpu_s >= args.cpu_seconds:
+            break
+    del src_cpu
+    if not args.no_cpu_baseline:
+        cpu = {"value": round(calls * alg / cpu_s / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "seconds": round(cpu_s, 2),
+               "sample": f"the whole workload, {calls} {args.op} calls; numpy, one thread pinned to one core; "
+                         f"CPU: {_cpu_model()}"}
     mism = int((got != want).sum())
     st = rla.stats()
+    kernel = patch_kernel_name(st["fast_launches"] > 0, inverse, p, eb)
+    name = patch_workload_name(args.op, shape, p, eb)
     line = {
         "metric": f"{args.op} (stage-5 space-to-depth) achieved HBM GB/s, bit-exact vs oracle",
         "value": round(alg / (wall / args.steps) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": {1: "u8", 2: "bf16-bits", 4: "f32-bits", 8: "u64"}[eb],
         "data": "synthetic (seeded random bit patterns)",
-        "config": {"workload": args.patch_workload, "shape": list(shape), "p": p, "elem_bytes": eb,
+        "config": {"workload": name, "key": args.patch_workload, "shape": list(shape), "p": p, "elem_bytes": eb,
                    "algorithmic_bytes_per_step": alg, "input_sets": rotate,
                    "outputs": "reused" if args.reuse_outputs else "fresh"},
-        "kernel": patch_kernel_name(st["fast_launches"] > 0, inverse, p, eb),
+        "kernel": kernel,
         "kernel_avg_us": round(kavg * 1e6, 2),
         "parity": {"compared_elements": int(got.size), "mismatching_elements": mism, "tolerance_ulp": 0},
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4), "traffic": None},
-        "cpu_baseline": None,
+                     "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, kernel)},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     if mism:
         sys.exit(1)
+
+
+def patch_workload_name(op: str, shape, p: int, elem_bytes: int) -> str:
+    dt = {1: "u8", 2: "bf16", 4: "f32", 8: "u64"}[elem_bytes]
+    return f"{op}_{dt}_{'x'.join(str(d) for d in shape)}_p{p}"
+
+
+def neox_cpu_baseline(w, q_np, k_np, pos_np, cache_np, target_s):
+    """The rotate-half oracle, untuned, on consecutive 256-token chunks of the same inputs (Q and K),
+    wrapping round to the first token, single thread, until about target_s seconds of CPU work are
+    done; scaled to the kernel's algorithmic bytes per token."""
+    import oracle.neox as nx
+
+    pin_one_core()
+    chunk, start, tokens = 256, 0, 0
+    t0 = time.perf_counter()
+    while True:
+        sl = slice(start, min(start + chunk, w.tokens))
+        for x in (q_np, k_np):
+            nx.neox_rope(x[sl], w.dtype, pos_np[sl], cache_np, w.cache_dtype)
+        tokens += sl.stop - sl.start
+        start = sl.stop % w.tokens
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(w.algorithmic_bytes() * tokens / w.tokens / dt / 1e9, 5), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{tokens} tokens ({tokens / w.tokens:.2f} passes over the {w.tokens}-token workload) in "
+                      f"{chunk}-token chunks, Q and K; numpy, one thread pinned to one core; CPU: {_cpu_model()}"}
 
 
 def cpu_baseline(w, gi, q_np, k_np, target_s):
@@ -540,10 +623,7 @@ def cpu_baseline(w, gi, q_np, k_np, target_s):
 
     import oracle
 
-    try:
-        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
-    except (AttributeError, OSError):
-        pass
+    pin_one_core()
     B, T, H, W, heads, D = w.shape(gi)
     t0 = time.perf_counter()
     tabs = oracle.grid_tables(T, H, W, w.split, w.base)

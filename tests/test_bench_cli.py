@@ -8,6 +8,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
+import pytest  # noqa: E402
+
 import bench  # noqa: E402
 
 
@@ -40,23 +42,37 @@ def test_defaults_per_op():
 def test_kernel_source_hash_ignores_comments(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("// a comment\nint x = 1;  // trailing\n/* block\ncomment */\nint y = 2;\n")
-    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src)])
-    h1 = bench.kernel_source_hash()
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", {"k": ("k.hip",)})
+    h1 = bench.kernel_source_hash("k")
     src.write_text("int x = 1;\n\n// other words\nint y = 2;\n")
-    assert bench.kernel_source_hash() == h1
+    assert bench.kernel_source_hash("k") == h1
     src.write_text("int x = 1;\nint y = 3;\n")
-    assert bench.kernel_source_hash() != h1
+    assert bench.kernel_source_hash("k") != h1
 
 
-def test_traffic_record_is_used_only_for_the_source_it_was_taken_on():
-    """bench.py reports the committed counter traffic only while the kernel source is the one the
-    counters were taken on (else null)."""
+def test_every_timed_kernel_hashes_its_own_sources():
+    for kernel, files in bench.KERNEL_SOURCES.items():
+        assert all(os.path.exists(os.path.join(bench.CSRC, f)) for f in files), kernel
+    assert bench.kernel_source_hash("patch_lds") == bench.kernel_source_hash("unpatch_lds")
+    assert bench.kernel_source_hash("rope_fast") != bench.kernel_source_hash("neox_fast")
+
+
+@pytest.mark.parametrize("kernel", sorted(bench.KERNEL_SOURCES))
+def test_traffic_record_is_used_only_for_the_source_it_was_taken_on(kernel):
+    """bench.py reports a kernel's committed counter traffic only for the workload and the kernel
+    source the counters were taken on (else null)."""
     import json
 
-    rec = json.load(open(bench.TRAFFIC_FILE))
-    assert 1.0 <= rec["traffic_over_algorithmic"] < 1.01
-    assert bench.measured_traffic("another workload") is None
-    if rec["kernel_source_sha256_16"] == bench.kernel_source_hash():
-        assert bench.measured_traffic(rec["workload"]) == rec["bytes_per_launch"]
+    path = bench.traffic_file(kernel)
+    if not os.path.exists(path):
+        assert bench.measured_traffic("any", kernel) is None
+        return
+    rec = json.load(open(path))
+    assert rec["kernel"] == kernel
+    assert 1.0 <= rec["traffic_over_algorithmic"] < 1.05
+    assert bench.measured_traffic("another workload", kernel) is None
+    if rec["kernel_source_sha256_16"] == bench.kernel_source_hash(kernel):
+        assert bench.measured_traffic(rec["workload"], kernel) == rec["bytes_per_launch"]
     else:
-        assert bench.measured_traffic(rec["workload"]) is None
+        assert bench.measured_traffic(rec["workload"], kernel) is None
