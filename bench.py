@@ -295,22 +295,7 @@ def main():
         got = got.view(torch.int16).numpy().view(np.uint16) if es == 2 else got.numpy()
         mism += int((got.view(want.dtype) != want).sum())
 
-    # copy-kernel ceiling on the same bytes and input sets (Q -> scratch, K -> scratch): one read
-    # stream and one write stream per launch, the fast kernel's launch shape and cache hints
-    dsts = [(torch.empty_like(q), torch.empty_like(k)) for _ in range(min(rotate, 2))]
-    reps = 10 * rotate
-    for i in range(3):
-        rla.copy_bytes(dsts[i % len(dsts)][0], sets[i % rotate][0])
-        rla.copy_bytes(dsts[i % len(dsts)][1], sets[i % rotate][1])
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for i in range(reps):
-        rla.copy_bytes(dsts[i % len(dsts)][0], sets[i % rotate][0])
-        rla.copy_bytes(dsts[i % len(dsts)][1], sets[i % rotate][1])
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = alg_bytes / (c0.elapsed_time(c1) / reps / 1e3) / 1e9
-    del dsts
+    copy_gbs = copy_ceiling(sets, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -409,6 +394,8 @@ def main_neox(args):
         mism += int((got.view(want.dtype) != want).sum())
     st = rla.stats()
     kernel = "neox_fast" if st["fast_launches"] else "neox_plain"
+    del outs
+    copy_gbs = copy_ceiling(sets, stream)
     cpu = None if args.no_cpu_baseline else neox_cpu_baseline(w, q_np, k_np, pos_np, cache_np, args.cpu_seconds)
     line = {
         "metric": "rotate-half RoPE with gathered cos/sin cache, achieved HBM GB/s, bit-exact vs oracle",
@@ -421,6 +408,7 @@ def main_neox(args):
                    "outputs": "reused" if args.reuse_outputs else "fresh"},
         "kernel": kernel,
         "kernel_avg_us": round(kavg * 1e6, 2),
+        "copy_ceiling_GBps": round(copy_gbs, 1),
         "parity": {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0},
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4),
@@ -535,7 +523,9 @@ def main_patch(args):
     wall = time.perf_counter() - t0
     kavg = e0.elapsed_time(e1) / args.steps / 1e3  # launches run back to back: no marker between them
     got = outs[-1].cpu().numpy().view(x_np.dtype)
-    del outs, sets
+    del outs
+    copy_gbs = copy_ceiling([(t,) for t in sets], stream)
+    del sets
     # the oracle on the whole workload: the parity reference for patchify and, repeated on one core
     # for about --cpu-seconds, the CPU baseline of either direction
     if inverse:
@@ -577,6 +567,7 @@ def main_patch(args):
                    "outputs": "reused" if args.reuse_outputs else "fresh"},
         "kernel": kernel,
         "kernel_avg_us": round(kavg * 1e6, 2),
+        "copy_ceiling_GBps": round(copy_gbs, 1),
         "parity": {"compared_elements": int(got.size), "mismatching_elements": mism, "tolerance_ulp": 0},
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, kernel)},
@@ -585,6 +576,32 @@ def main_patch(args):
     print(json.dumps(line), flush=True)
     if mism:
         sys.exit(1)
+
+
+def copy_ceiling(sets, stream, reps_per_set: int = 10) -> float:
+    """GB/s of the library's plain copy kernel on the same input sets: one step copies each
+    tensor of one set into a scratch tensor of its size (one read stream and one write stream per
+    launch, the fast kernels' launch shape and cache hints), timed like the kernel; bytes = each
+    tensor read once and written once."""
+    import torch
+
+    import rope_ltx3drope_amd as rla
+
+    bytes_per_step = sum(2 * t.numel() * t.element_size() for t in sets[0])
+
+    dsts = [tuple(torch.empty_like(t) for t in sets[0]) for _ in range(min(len(sets), 2))]
+    for i in range(3):
+        for d, t in zip(dsts[i % len(dsts)], sets[i % len(sets)]):
+            rla.copy_bytes(d, t)
+    reps = reps_per_set * len(sets)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for i in range(reps):
+        for d, t in zip(dsts[i % len(dsts)], sets[i % len(sets)]):
+            rla.copy_bytes(d, t)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    return bytes_per_step / (c0.elapsed_time(c1) / reps / 1e3) / 1e9
 
 
 def patch_workload_name(op: str, shape, p: int, elem_bytes: int) -> str:
