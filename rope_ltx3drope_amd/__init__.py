@@ -257,7 +257,10 @@ def forward_pair(q, k, split: Sequence[int], base: float = 10000.0, q_out=None, 
     if grid is None:
         t0, h0, w0 = offsets or (0, 0, 0)
         grid = (T + t0, H + h0, W + w0)
-    with tables_build(*grid, split, base, device=q.device.index or 0, stream=stream) as tabs:
+    if not q.is_cuda:
+        raise Ltx3dRopeUnsupported("NOT_DEVICE_PTR")
+    device = q.device.index if q.device.index is not None else _torch().cuda.current_device()
+    with tables_build(*grid, split, base, device=device, stream=stream) as tabs:
         return apply_qk(q, k, tabs, q_out, k_out, stream, offsets, inplace)
 
 
@@ -306,6 +309,8 @@ def neox_apply_qk(q, k, positions, cache, q_out=None, k_out=None, inplace: bool 
     torch = _torch()
     _neox_marshal(q, k, positions, cache, q_out, k_out)
     if inplace:
+        if (q_out is not None and q_out is not q) or (k_out is not None and k_out is not k):
+            raise ValueError("inplace=True writes into q and k")
         q_out, k_out = q, k
     if q_out is None:
         q_out = torch.empty_like(q)
@@ -354,6 +359,8 @@ def patchify(x, p: int, out=None, stream=None):
 def unpatchify(y, p: int, out=None, stream=None):
     """Inverse of patchify: (B, C*p*p, F, H/p, W/p) -> (B, C, F, H, W)."""
     torch = _torch()
+    if p < 1:
+        raise ValueError("p must be positive")
     if y.dim() != 5 or not y.is_cuda or not y.is_contiguous() or int(y.shape[1]) % (p * p):
         raise Ltx3dRopeUnsupported("SHAPE_MISMATCH")
     B, Cpp, F, Hp, Wp = (int(s) for s in y.shape)

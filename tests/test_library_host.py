@@ -490,3 +490,20 @@ def test_dit_freq_grid_rejects_bad_arguments():
         assert L.ltx3drope_dit_freq_grid(*args, 1, None, 0, None, ctypes.byref(n)) == _lib.E_INVALID
     assert L.ltx3drope_dit_freq_grid(1e4, 64, 2, 1, None, 0, None, ctypes.byref(n)) == _lib.E_INVALID  # NULL out
     assert L.ltx3drope_dit_freq_grid(1e4, 1, 2, 1, None, 0, None, ctypes.byref(n)) == _lib.OK and n.value == 0
+
+
+def test_binding_refuses_host_tensors_and_bad_patch_sizes_before_any_call():
+    """The binding's own argument checks (no library call is made for these)."""
+    import torch
+
+    q = torch.zeros(1, 2, 2, 2, 1, 6)
+    with pytest.raises(rla.Ltx3dRopeUnsupported) as e:
+        rla.forward_pair(q, q.clone(), (2, 2, 2))
+    assert e.value.reason == "NOT_DEVICE_PTR"
+    assert rla.can_use(q, q.clone(), None) == (False, "NOT_DEVICE_PTR")
+    with pytest.raises(rla.Ltx3dRopeUnsupported):
+        rla.patchify(torch.zeros(1, 1, 1, 4, 4), 2)  # host tensor
+    for p in (0, -2):
+        with pytest.raises(ValueError):
+            rla.unpatchify(torch.zeros(1, 4, 1, 2, 2), p)
+    assert rla.stats()["rejected"] == 0  # nothing reached the library
