@@ -23,13 +23,14 @@
 //    (8 bf16 or 4 fp32 values, i.e. 4 or 2 pairs): the first half of the grid
 //    covers Q, the second half K.  When a token's heads*head_dim row is a whole
 //    number of wavefronts, the token -> (t, h, w) decode runs once per
-//    wavefront on scalar values.  The (cos, sin) row segment of the vector
-//    comes from the packed tables with 16-byte loads that stay in the L1/L2
-//    caches (the tables are tens of KB); Q and K stream through with
-//    non-temporal 16-byte loads and streaming (sc1 | nt) 16-byte stores; bf16
-//    results are packed with the hardware's round-to-nearest-even conversion
-//    (v_cvt_pk_bf16_f32).  Measured on MI355X, this shape streams faster than
-//    a persistent grid with LDS-staged tables and several vectors per lane.
+//    wavefront on scalar values and the wavefront assembles the token's
+//    (cos, sin) row in LDS; otherwise each lane reads its vector's row segment
+//    from the packed tables, which stay in the L1/L2 caches (they are tens of
+//    KB).  Q and K stream through with non-temporal 16-byte loads and
+//    streaming (sc1 | nt) 16-byte stores; bf16 results are packed with the
+//    hardware's round-to-nearest-even conversion (v_cvt_pk_bf16_f32).
+//    Measured on MI355X, this shape streams faster than a persistent grid with
+//    LDS-staged tables and several vectors per lane.
 #include <hip/hip_runtime.h>
 
 #include <map>
@@ -186,20 +187,28 @@ struct FastArgs {
     uint32_t V;        // 16-B vectors per head
     uint32_t N, HW, W;
     uint32_t PT, PH;   // pairs in the t and h chunks
-    uint32_t rowT4, rowH4, rowW4;  // float4 per table row of each section (ALIGNED)
-    uint32_t offH4, offW4;         // first float4 of the h and w sections (ALIGNED)
+    uint32_t rowT4, rowH4, rowW4;  // float4 per table row of each section (kTabAligned)
+    uint32_t offH4, offW4;         // first float4 of the h and w sections (kTabAligned)
     uint32_t PW;                   // pairs in the w chunk
     uint32_t offH2, offW2;         // first (cos, sin) pair of the h and w sections
     uint32_t t_off, h_off, w_off;  // global coordinate of the tensor's first frame / row / column
     FastDiv div_HV, div_V, div_N, div_HW, div_W;  // the token decode's divisors (fastdiv.h)
 };
 
-// PPV pairs per 16-B vector: 4 for bf16, 2 for fp32.  ALIGNED: the t and h chunk
-// widths are multiples of PPV pairs (so is the w chunk, as head_dim is a whole
-// number of vectors), so a vector never straddles two chunks and its PPV
-// (cos, sin) pairs are PPV/2 consecutive float4 of one row.  Otherwise (any even
-// split) each pair finds its chunk and row on its own and loads its (cos, sin)
-// as one float2.
+// PPV pairs per 16-B vector: 4 for bf16, 2 for fp32.  How a vector finds its PPV
+// (cos, sin) pairs (TAB):
+//  * kTabAligned: the t and h chunk widths are multiples of PPV pairs (so is the
+//    w chunk, as head_dim is a whole number of vectors), so a vector never
+//    straddles two chunks and its pairs are PPV/2 consecutive float4 of one row.
+//  * kTabRow (any even split, one token per wavefront, head_dim <= 1024): the
+//    wavefront first assembles its token's head_dim/2 pairs -- t row, then h
+//    row, then w row -- in LDS, one float2 per lane and step; each lane then
+//    reads its PPV pairs as PPV/2 float4.  One 8-byte table load per lane
+//    instead of one per pair (or two 16-byte loads): measured on MI355X, any
+//    split then streams at the copy kernel's rate, and aligned splits about
+//    1 % faster than with kTabAligned's direct loads.
+//  * kTabPair (any even split, any token layout): each pair finds its chunk and
+//    row on its own and loads its (cos, sin) as one float2.
 //
 // Grid: 2 * ceil(vectors / 64) workgroups of one wavefront.  The first half of
 // the grid rotates Q, the second half K, so that while the grid runs the memory
@@ -217,8 +226,12 @@ struct FastArgs {
 // streaming store (sc1 | nt): every byte is touched exactly once, so the streams
 // should not displace other data from the caches (measured: +3 to +10 % on the
 // 0.8-6.8 GB workloads for the hints, about +1 % more for the store policy).
-template <bool BF16, bool WAVE_TOKEN, bool ALIGNED>
+enum : int { kTabAligned = 0, kTabPair = 1, kTabRow = 2 };
+constexpr uint32_t kTabRowMaxBytes = 4096;  // kTabRow's LDS row: head_dim <= 1024
+
+template <bool BF16, bool WAVE_TOKEN, int TAB>
 __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
+    static_assert(TAB != kTabRow || WAVE_TOKEN, "the LDS row needs one token per wavefront");
     constexpr uint32_t PPV = BF16 ? 4 : 2;
     const uint32_t half = gridDim.x >> 1;
     const bool second = blockIdx.x >= half;  // wave-uniform
@@ -247,7 +260,7 @@ __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
     const uint32_t j0 = fast_mod(u, a.div_V) * PPV;  // first pair of this vector inside its head
     const u32x4 x = __builtin_nontemporal_load(src + g);
     float c[PPV], s[PPV];
-    if constexpr (ALIGNED) {
+    if constexpr (TAB == kTabAligned) {
         uint32_t idx;
         if (j0 < a.PT) {
             idx = t * a.rowT4 + j0 / 2;
@@ -259,6 +272,31 @@ __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
 #pragma unroll
         for (uint32_t r = 0; r < PPV / 2; ++r) {
             const f32x4 cs = a.tab[idx + r];  // (c, s) of two consecutive pairs
+            c[2 * r] = cs.x;
+            s[2 * r] = cs.y;
+            c[2 * r + 1] = cs.z;
+            s[2 * r + 1] = cs.w;
+        }
+    } else if constexpr (TAB == kTabRow) {
+        extern __shared__ __align__(16) f32x2 tab_row[];  // head_dim/2 pairs of this token
+        const f32x2* tab2 = reinterpret_cast<const f32x2*>(a.tab);
+        const uint32_t pairs = a.V * PPV;  // head_dim / 2
+        for (uint32_t j = threadIdx.x; j < pairs; j += kFastBlock) {
+            uint32_t idx;
+            if (j < a.PT) {
+                idx = t * a.PT + j;
+            } else if (j < a.PT + a.PH) {
+                idx = a.offH2 + h * a.PH + (j - a.PT);
+            } else {
+                idx = a.offW2 + w * a.PW + (j - a.PT - a.PH);
+            }
+            tab_row[j] = tab2[idx];
+        }
+        __syncthreads();  // one wavefront: waits for its own LDS writes
+        const f32x4* row4 = reinterpret_cast<const f32x4*>(tab_row) + j0 / 2;
+#pragma unroll
+        for (uint32_t r = 0; r < PPV / 2; ++r) {
+            const f32x4 cs = row4[r];
             c[2 * r] = cs.x;
             s[2 * r] = cs.y;
             c[2 * r + 1] = cs.z;
@@ -386,16 +424,23 @@ bool fast_supported(const Problem& p) {
     return (p.D * es) % 16 == 0;  // head rows are whole 16-byte vectors; any even split
 }
 
-template <bool ALIGNED>
-hipError_t launch_fast_split(const FastArgs& a, bool bf16, bool wave_token, uint32_t blocks, hipStream_t stream) {
-    if (bf16 && wave_token)
-        hipLaunchKernelGGL((rope_fast<true, true, ALIGNED>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    else if (bf16)
-        hipLaunchKernelGGL((rope_fast<true, false, ALIGNED>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    else if (wave_token)
-        hipLaunchKernelGGL((rope_fast<false, true, ALIGNED>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    else
-        hipLaunchKernelGGL((rope_fast<false, false, ALIGNED>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+template <int TAB>
+hipError_t launch_fast_tab(const FastArgs& a, bool bf16, bool wave_token, uint32_t blocks, size_t lds,
+                           hipStream_t stream) {
+    if constexpr (TAB == kTabRow) {
+        if (bf16)
+            hipLaunchKernelGGL((rope_fast<true, true, kTabRow>), dim3(blocks), dim3(kFastBlock), lds, stream, a);
+        else
+            hipLaunchKernelGGL((rope_fast<false, true, kTabRow>), dim3(blocks), dim3(kFastBlock), lds, stream, a);
+    } else if (bf16 && wave_token) {
+        hipLaunchKernelGGL((rope_fast<true, true, TAB>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    } else if (bf16) {
+        hipLaunchKernelGGL((rope_fast<true, false, TAB>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    } else if (wave_token) {
+        hipLaunchKernelGGL((rope_fast<false, true, TAB>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((rope_fast<false, false, TAB>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
@@ -439,9 +484,12 @@ hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
     const bool bf16 = p.dtype == LTX3DROPE_DTYPE_BF16;
     const uint32_t ppv = 8u / es;
     const bool aligned = p.PT % ppv == 0 && p.PH % ppv == 0;
+    const size_t row_bytes = size_t(p.D / 2) * 8;  // kTabRow's LDS: (cos, sin) of every pair of a head
     (void)device;
-    if (aligned) return launch_fast_split<true>(a, bf16, wave_token, blocks, stream);
-    return launch_fast_split<false>(a, bf16, wave_token, blocks, stream);
+    if (wave_token && row_bytes <= kTabRowMaxBytes)
+        return launch_fast_tab<kTabRow>(a, bf16, true, blocks, row_bytes, stream);
+    if (aligned) return launch_fast_tab<kTabAligned>(a, bf16, wave_token, blocks, 0, stream);
+    return launch_fast_tab<kTabPair>(a, bf16, wave_token, blocks, 0, stream);
 }
 
 hipError_t launch_plain(const Problem& p, hipStream_t stream, int device) {

@@ -135,6 +135,13 @@ RAGGED = [
     ((1, 2, 3, 4, 40, 128), (32, 48, 48), oracle.BF16),   # 640 vectors per token
     ((1, 2, 2, 3, 80, 96), (32, 32, 32), oracle.BF16),    # 960 vectors per token
     ((1, 1, 2, 2, 3, 20), (8, 8, 4), oracle.BF16),        # head row not a whole 16-byte vector
+    # splits whose chunks are not whole vectors, one token per wavefront: the LDS-assembled table row
+    ((1, 2, 3, 4, 16, 96), (30, 34, 32), oracle.BF16),
+    ((1, 3, 2, 5, 24, 128), (40, 44, 44), oracle.BF16),
+    ((1, 2, 3, 3, 32, 48), (14, 18, 16), oracle.F32),
+    ((1, 2, 2, 3, 4, 256), (86, 86, 84), oracle.BF16),    # 128 pairs: two per lane
+    ((2, 2, 1, 3, 2, 1024), (342, 342, 340), oracle.BF16),  # the largest row the LDS holds (4 KB)
+    ((1, 1, 2, 2, 32, 1040), (346, 348, 346), oracle.BF16),  # larger: per-pair table loads
 ]
 
 
@@ -528,6 +535,7 @@ SHARDS = [
     ((4, 5, 12), (1, 4, 5, 5, 2, 48), (0, 0, 7), (16, 16, 16), oracle.F32),
     ((6, 8, 9), (2, 2, 3, 4, 8, 64), (3, 2, 5), (16, 24, 24), oracle.BF16),
     ((6, 8, 9), (1, 2, 3, 4, 3, 12), (1, 4, 2), (2, 6, 4), oracle.BF16),  # plain kernel only
+    ((6, 8, 9), (1, 2, 3, 4, 16, 96), (2, 3, 4), (30, 34, 32), oracle.BF16),  # LDS-assembled table row
 ]
 
 
