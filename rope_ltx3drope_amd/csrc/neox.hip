@@ -281,16 +281,18 @@ NeoxArgs make_args(const NeoxProblem& p, unsigned* errors) {
 
 }  // namespace
 
-// Half head rows of whole 16-B vectors (at most 64 of them) and 16-B aligned
-// tensors.  Then every cache segment a vector needs (8 or 4 values, of 2 or 4
-// bytes) is naturally aligned: the row offset p*D and the half offset D/2 are
-// multiples of the segment length.
+// Half head rows of whole 16-B vectors (at most 64 of them), 16-B aligned
+// tensors and at most 2^25 - 1 tokens (two 64-lane workgroups per token, and a
+// grid holds fewer than 2^32 work-items).  Then every cache segment a vector
+// needs (8 or 4 values, of 2 or 4 bytes) is naturally aligned: the row offset
+// p*D and the half offset D/2 are multiples of the segment length.
 bool neox_fast_supported(const NeoxProblem& p) {
     const uint32_t es = p.dtype == LTX3DROPE_DTYPE_F32 ? 4u : 2u;
     for (const void* ptr : {p.q, p.k, static_cast<const void*>(p.q_out), static_cast<const void*>(p.k_out), p.cache})
         if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return false;
     const uint64_t heads = p.q_heads > p.k_heads ? p.q_heads : p.k_heads;
     if (heads * p.D * es >= (uint64_t(1) << 31)) return false;  // a token's row is addressed with 32-bit offsets
+    if (uint64_t(p.tokens) * 2 * kBlock > 0xffffffffull) return false;  // the grid's work-items must fit in 32 bits
     return (p.D / 2 * es) % 16 == 0 && p.D / 2 * es / 16 <= 64;
 }
 

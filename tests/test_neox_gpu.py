@@ -187,3 +187,28 @@ def test_random_configurations(seed):
             assert_bitexact(gq, nx.neox_rope(q, dtype, pos, cache, cdt), dtype, f"q {w} path {path}")
             assert_bitexact(gk, nx.neox_rope(k, dtype, pos, cache, cdt), dtype, f"k {w} path {path}")
     assert rla.neox_position_errors(0) == 0
+
+
+def test_more_tokens_than_the_fast_grid_holds_use_the_plain_kernel():
+    """2^25 + 3 tokens of one head of 16 bf16 values: two 64-lane workgroups per token would need
+    2^32 work-items or more, so the call runs on the plain kernel; sampled tokens (the last
+    included) against the oracle.  Q and K come from torch's seeded device generator."""
+    tokens, D, maxp = (1 << 25) + 3, 16, 1000
+    g = torch.Generator(device=DEV).manual_seed(2024)
+    log("2^25 + 3 tokens: generating inputs on the device")
+    dq = torch.randn(tokens, 1, D, generator=g, device=DEV).to(torch.bfloat16)
+    dk = torch.randn(tokens, 1, D, generator=g, device=DEV).to(torch.bfloat16)
+    dpos = torch.randint(0, maxp, (tokens,), generator=g, device=DEV, dtype=torch.int64)
+    w = workloads.NeoxWorkload("big", oracle.BF16, 16, 1, 1, D, maxp, oracle.F32, "random", 31)
+    _, _, _, cache = workloads.generate_neox(w)
+    qo, ko = rla.neox_apply_qk(dq, dk, dpos, to_dev(cache, oracle.F32))
+    torch.cuda.synchronize()
+    s = rla.stats()
+    assert s["plain_launches"] == 1 and s["fast_launches"] == 0
+    assert rla.neox_position_errors(0) == 0
+    ids = np.unique(np.concatenate([workloads.sample_tokens(tokens, 2000, seed=5), [tokens - 2, tokens - 3]]))
+    idx = torch.from_numpy(ids).to(DEV)
+    pos = dpos[idx].cpu().numpy()
+    for x, out in ((dq, qo), (dk, ko)):
+        want = nx.neox_rope(to_host(x[idx], oracle.BF16), oracle.BF16, pos, cache, oracle.F32)
+        assert_bitexact(to_host(out[idx], oracle.BF16), want, oracle.BF16, "sampled tokens")
