@@ -187,7 +187,9 @@ int ltx3drope_can_use(const void* q_out, const void* k_out, const void* q, const
  * call verified; equal -> the fast path is trusted, unequal -> permanent
  * fallback to the plain path for that configuration).  The gate's
  * configuration key is (device, dtype, B, T, H, W, heads, head_dim, dim_t,
- * dim_h, dim_w).
+ * dim_h, dim_w).  The first verification on a device allocates that device's
+ * 256-byte counter, kept until the process ends: E_NOMEM if the device is out
+ * of memory, E_HIP for any other failed HIP call or launch.
  */
 int ltx3drope_apply_qk(void* q_out, void* k_out, const void* q, const void* k, int dtype,
                        int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
@@ -253,7 +255,10 @@ int ltx3drope_apply_qk_shard(void* q_out, void* k_out, const void* q, const void
  * Reasons: NULLPTR, DTYPE (q or cache dtype), NONPOSITIVE_DIM, SPLIT_ODD
  * (odd head_dim), ALIGN (element alignment; positions 8 B), OVERLAP,
  * TOO_LARGE (a tensor of 2^31 elements or more), NOT_DEVICE_PTR,
- * TABLE_DEVICE (pointers on different devices), EXTENT.
+ * TABLE_DEVICE (pointers on different devices), EXTENT.  apply_qk returns
+ * E_UNSUPPORTED for any of these; the first call on a device allocates the
+ * device's 256-byte counter (E_NOMEM when out of memory, E_HIP for another
+ * HIP failure), and a failed launch gives E_HIP.
  */
 int ltx3drope_neox_can_use(const void* q_out, const void* k_out, const void* q, const void* k, int dtype,
                            int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim,
@@ -279,7 +284,9 @@ int ltx3drope_neox_position_errors(int device, int reset, int64_t* count);
  * multiple of p, elem_bytes not 1/2/4/8, NULL pointers.  E_UNSUPPORTED: 2^31
  * elements or more, pointers not aligned to one element, overlapping tensors,
  * not device memory of one device, or allocations smaller than the tensors.
- * Asynchronous on `stream`.
+ * Asynchronous on `stream`.  E_NOMEM / E_HIP: the device's first call could not
+ * allocate the library's 256-byte per-device counter block; E_HIP: a failed
+ * launch.
  */
 int ltx3drope_patchify(void* y, const void* x, int elem_bytes, int64_t B, int64_t C, int64_t F, int64_t H,
                        int64_t W, int64_t p, void* stream);

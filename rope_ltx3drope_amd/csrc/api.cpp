@@ -105,9 +105,10 @@ int device_res(int device, DeviceRes** out) {
     DeviceRes& r = g_dev[device];
     if (r.counter == nullptr) {
         void* mem = nullptr;
-        if (hipMalloc(&mem, 256) != hipSuccess) {
+        const hipError_t e = hipMalloc(&mem, 256);
+        if (e != hipSuccess) {
             (void)hipGetLastError();
-            return LTX3DROPE_E_NOMEM;
+            return e == hipErrorOutOfMemory ? LTX3DROPE_E_NOMEM : LTX3DROPE_E_HIP;
         }
         // both counters start at zero (cleared by a kernel, then waited for once)
         if (launch_zero_u32(static_cast<unsigned*>(mem), nullptr) != hipSuccess ||

@@ -1,6 +1,7 @@
 // Sanitizer driver for the library's host code (cache, reference counts, precheck,
 // options, statistics, the DiT frequency grid), run in host-table mode from several
-// threads.  Exit status 0 and no sanitizer report mean success.
+// threads, then allocation-failure injection against an emulated device.  Exit status 0
+// and no sanitizer report mean success.
 #include <atomic>
 #include <cmath>
 #include <cstdio>
@@ -9,9 +10,14 @@
 #include <thread>
 #include <vector>
 
+#include <hip/hip_runtime_api.h>
+
 #include "ltx3drope.h"
 
 extern std::atomic<long> g_hip_calls;
+extern std::atomic<int> g_emulate;
+extern std::atomic<int> g_malloc_fail;
+extern std::atomic<long> g_live_allocs;
 
 #define CHECK(cond)                                                       \
     do {                                                                  \
@@ -134,6 +140,38 @@ int main(int argc, char** argv) {
     CHECK(s.tables_alive == 0);  // every table freed once the cache and all holders let go
     CHECK(s.fast_launches == 0 && s.plain_launches == 0);
     CHECK(g_hip_calls.load() == 0);  // host-table mode never reaches HIP
+
+    // Device mode against an emulated device 0, with hipMalloc failures injected: a failed table
+    // upload or counter allocation returns E_NOMEM (out of memory) or E_HIP (any other error),
+    // leaves nothing behind, and the next successful build is cached as usual.
+    CHECK(ltx3drope_set_option(LTX3DROPE_OPT_HOST_TABLES, 0) == LTX3DROPE_OK);
+    CHECK(ltx3drope_stats_reset() == LTX3DROPE_OK);
+    g_emulate = 1;
+    int64_t count = -1;
+    g_malloc_fail = hipErrorOutOfMemory;
+    t = reinterpret_cast<ltx3drope_tables_t>(&count);
+    CHECK(ltx3drope_tables_build(0, 2, 3, 4, 8, 8, 8, 10000.0, nullptr, &t) == LTX3DROPE_E_NOMEM && t == nullptr);
+    CHECK(ltx3drope_neox_position_errors(0, 0, &count) == LTX3DROPE_E_NOMEM && count == -1);
+    g_malloc_fail = hipErrorInvalidValue;
+    CHECK(ltx3drope_tables_build(0, 2, 3, 4, 8, 8, 8, 10000.0, nullptr, &t) == LTX3DROPE_E_HIP && t == nullptr);
+    CHECK(ltx3drope_neox_position_errors(0, 0, &count) == LTX3DROPE_E_HIP && count == -1);
+    CHECK(ltx3drope_stats(&s) == LTX3DROPE_OK);
+    CHECK(s.tables_alive == 0 && s.cache_live == 0 && s.cache_misses == 0 && g_live_allocs.load() == 0);
+    g_malloc_fail = 0;
+    ltx3drope_tables_t t2 = nullptr;
+    CHECK(ltx3drope_tables_build(0, 2, 3, 4, 8, 8, 8, 10000.0, nullptr, &t) == LTX3DROPE_OK && t != nullptr);
+    CHECK(ltx3drope_tables_build(0, 2, 3, 4, 8, 8, 8, 10000.0, nullptr, &t2) == LTX3DROPE_OK && t2 == t);
+    std::vector<float> c(4), sn(4);
+    CHECK(ltx3drope_tables_read(t, c.data(), sn.data(), nullptr, nullptr, nullptr, nullptr) == LTX3DROPE_E_HIP);
+    CHECK(ltx3drope_stats(&s) == LTX3DROPE_OK);
+    CHECK(s.tables_alive == 1 && s.cache_live == 1 && s.cache_misses == 1 && s.cache_hits == 1);
+    CHECK(g_live_allocs.load() == 1);
+    CHECK(ltx3drope_tables_release(t) == LTX3DROPE_OK && ltx3drope_tables_release(t2) == LTX3DROPE_OK);
+    CHECK(ltx3drope_cache_clear() == LTX3DROPE_OK);
+    CHECK(ltx3drope_stats(&s) == LTX3DROPE_OK);
+    CHECK(s.tables_alive == 0 && g_live_allocs.load() == 0);
+    g_emulate = 0;
+
     std::printf("host sanitizer driver: %d threads x %d iterations, %lld hits, %lld misses, %lld evictions\n",
                 threads, iters, static_cast<long long>(s.cache_hits), static_cast<long long>(s.cache_misses),
                 static_cast<long long>(s.cache_evictions));

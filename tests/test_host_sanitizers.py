@@ -6,7 +6,10 @@ stand-ins for the HIP runtime and the kernel launchers (tests/host_sanitize/stub
 driven by tests/host_sanitize/driver.cpp: eight threads build, read, hold and release table
 sets of 24 grids through the 16-entry cache (evictions while handles are held), run the
 precheck, refused launches, statistics, cache clears and the DiT frequency grid, all in
-host-table mode.  At the end every table must be freed and no HIP stand-in called.
+host-table mode.  At the end every table must be freed and no HIP stand-in called.  Then,
+against stand-ins that emulate a device 0 with host memory, injected hipMalloc failures must
+give E_NOMEM (out of memory) or E_HIP (another error) from the table upload and the device
+counter's allocation, leave no table or allocation behind, and a later build must succeed.
 """
 from __future__ import annotations
 
