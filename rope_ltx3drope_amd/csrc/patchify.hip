@@ -8,17 +8,18 @@
 // movement, so the result is bit-exact for any element type; the kernels move
 // elements of 1, 2, 4 or 8 bytes.
 //
-//  * patch_lds<T, P> / unpatch_lds<T, P>: a wavefront owns P*64 consecutive
-//    16-byte vectors of the unpatched tensor, taken in (b, c, height offset, f,
-//    patch row, vector) order for patchify and (b, c, f, height offset, patch
-//    row, vector) order for the inverse, which are exactly 64 consecutive packed
-//    vectors of each of the P width-offset planes that share (b, c, height
-//    offset).  The
-//    wavefront reads one side with P contiguous 1 KB loads, regroups the
-//    elements by width offset through P KB of LDS, and writes the other side
-//    with P contiguous 1 KB stores.  Used whenever a 16-byte
-//    vector splits evenly across the P width offsets (16/sizeof(T) a multiple
-//    of p: bf16 with p = 2, 4, 8; fp32 with p = 2, 4).
+//  * patch_lds<T, P>: a wavefront owns P*64 consecutive 16-byte vectors of the
+//    unpatched tensor, taken in (b, c, height offset, f, patch row, vector)
+//    order, which are exactly 64 consecutive packed vectors of each of the P
+//    width-offset planes that share (b, c, height offset).  The wavefront reads
+//    them with P contiguous 1 KB loads, regroups the elements by width offset
+//    through P KB of LDS, and writes P contiguous 1 KB stores, one per plane.
+//  * unpatch_lds<T, P>: the inverse, on 128 unpatched vectors per wavefront in
+//    (b, c, f, height offset, patch row, vector) order: two loads per lane that
+//    each cover whole runs of 128/P packed vectors, two contiguous 1 KB stores.
+//  Both are used whenever a 16-byte vector splits evenly across the P width
+//  offsets (16/sizeof(T) a multiple of p: bf16 with p = 2, 4, 8; fp32 with
+//  p = 2, 4).
 //  * patch_fast<T, P, INVERSE>: one thread per group of P consecutive 16-byte
 //    vectors of an unpatched row, transposed in registers; covers the remaining
 //    fast case (fp32, p = 8), in both directions.
@@ -31,9 +32,8 @@
 // threads in unpatched-row order wrote each 480-byte packed row piecemeal
 // (4.1 TB/s); the (b, c, f, height offset, patch row) order with a register
 // transpose reached 5.5 TB/s (patchify) and a per-lane gather 6.0 TB/s
-// (unpatchify); the LDS-staged kernels, whose every global instruction is a
-// contiguous 1 KB, reach 5.9-6.0 and 6.2 TB/s with non-temporal loads and
-// streaming (sc1 | nt) stores.
+// (unpatchify); the LDS-staged kernels reach 5.9-6.0 (patchify) and 6.5 TB/s
+// (unpatchify) with non-temporal loads and streaming (sc1 | nt) stores.
 #include <hip/hip_runtime.h>
 
 #include "fastdiv.h"
@@ -243,33 +243,45 @@ __global__ void __launch_bounds__(kBlock) patch_lds(PatchArgs a) {
     }
 }
 
-// The inverse: the wavefront reads its 64 packed vectors of each width-offset plane into
-// lds[pw], then assembles its P*64 unpatched vectors.
+// The inverse works on half as much per wavefront: wavefront w owns unpatched vectors
+// [w*128, (w+1)*128) and packed vectors [w*128/P, (w+1)*128/P) of every width-offset plane.
+// Lane l reads the wavefront's packed vectors l and l + 64 (plane-major: plane (l + 64r) /
+// (128/P)) into LDS, then assembles unpatched vectors l and l + 64.  Each load instruction then
+// covers whole 128/P-vector runs of 64*P/128 planes, each store instruction a contiguous 1 KB.
+// Measured on a 121-frame 544 x 960 bf16 clip, p = 4: 117.1 us against 122.0 us for the
+// P*64-vector wavefronts of patch_lds (and 117.8 us with 64 vectors per wavefront).
+constexpr uint32_t kUnpatchVectors = 2 * kBlock;  // unpatched 16-byte vectors per wavefront
+
 template <typename T, int P>
 __global__ void __launch_bounds__(kBlock) unpatch_lds(PatchArgs a) {
     constexpr int E = 16 / sizeof(T);
     constexpr int K = E / P;
     static_assert(K * P == E, "a vector must split evenly across the width offsets");
+    constexpr uint32_t U = kUnpatchVectors;
+    constexpr uint32_t PV = U / P;  // packed vectors of each plane per wavefront
     typedef typename Chunk<K * sizeof(T)>::type Ch;
-    __shared__ __align__(16) T lds[P][kBlock * E];
+    __shared__ __align__(16) T lds[P][PV * E];
     const uint32_t lane = threadIdx.x;
-    const uint32_t O = blockIdx.x * kBlock + lane;
+    const uint32_t first = blockIdx.x * U;
+    const uint32_t left = a.groups - first;
+    const uint32_t valid = left < U ? left : U;  // a multiple of P: rows are whole groups of P vectors
     const T* src = static_cast<const T*>(a.src);
-    if (O < a.groups / P) {
-        const uint64_t off0 = packed_offset0<P, E, false>(a, O);
-        const uint64_t plane_stride = static_cast<uint64_t>(P) * a.F * (a.H / P) * (a.W / P);
+    const uint64_t plane_stride = static_cast<uint64_t>(P) * a.F * (a.H / P) * (a.W / P);
 #pragma unroll
-        for (int pw = 0; pw < P; ++pw)
-            reinterpret_cast<u32x4*>(&lds[pw][0])[lane] =
-                __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off0 + pw * plane_stride));
+    for (uint32_t r = 0; r < U / kBlock; ++r) {
+        const uint32_t idx = r * kBlock + lane;
+        const uint32_t pw = idx / PV, j = idx % PV;
+        if (j < valid / P) {
+            const uint64_t off = packed_offset0<P, E, false>(a, blockIdx.x * PV + j) + pw * plane_stride;
+            reinterpret_cast<u32x4*>(&lds[pw][0])[j] =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off));
+        }
     }
     __syncthreads();
-    const uint32_t first = blockIdx.x * (P * kBlock);
 #pragma unroll
-    for (int r = 0; r < P; ++r) {
-        const uint32_t I = first + r * kBlock + lane;
-        if (I >= a.groups) break;
+    for (uint32_t r = 0; r < U / kBlock; ++r) {
         const uint32_t li = r * kBlock + lane;
+        if (li >= valid) break;
         Vec<T> v;
 #pragma unroll
         for (int pw = 0; pw < P; ++pw) {
@@ -279,7 +291,7 @@ __global__ void __launch_bounds__(kBlock) unpatch_lds(PatchArgs a) {
 #pragma unroll
             for (int k = 0; k < K; ++k) v.e[k * P + pw] = ch[k];
         }
-        store_out<T>(a, unpatched_offset<P, E, false>(a, I), __builtin_bit_cast(u32x4, v));
+        store_out<T>(a, unpatched_offset<P, E, false>(a, first + li), __builtin_bit_cast(u32x4, v));
     }
 }
 
@@ -336,8 +348,10 @@ hipError_t launch_plain_t(PatchArgs a, uint32_t elem_bytes, hipStream_t stream, 
 }
 
 template <typename T>
-hipError_t launch_lds_t(PatchArgs a, uint32_t P, bool inverse, uint32_t blocks, hipStream_t stream) {
+hipError_t launch_lds_t(PatchArgs a, uint32_t P, bool inverse, hipStream_t stream) {
     constexpr uint32_t E = 16 / sizeof(T);
+    const uint32_t per_block = inverse ? kUnpatchVectors : P * kBlock;  // unpatched vectors per wavefront
+    const uint32_t blocks = (a.groups + per_block - 1) / per_block;
     switch (P) {
         case 2:
             if (inverse) hipLaunchKernelGGL((unpatch_lds<T, 2>), dim3(blocks), dim3(kBlock), 0, stream, a);
@@ -393,9 +407,8 @@ hipError_t launch_patch(const PatchProblem& p, bool inverse, hipStream_t stream,
             a.div_WpE = make_fastdiv(p.W / p.p / E);
             a.div_Hp = make_fastdiv(p.H / p.p);
             a.div_F = make_fastdiv(p.F);
-            const uint32_t blocks = (a.groups + p.p * kBlock - 1) / (p.p * kBlock);
-            return p.elem_bytes == 2 ? launch_lds_t<uint16_t>(a, p.p, inverse, blocks, stream)
-                                     : launch_lds_t<uint32_t>(a, p.p, inverse, blocks, stream);
+            return p.elem_bytes == 2 ? launch_lds_t<uint16_t>(a, p.p, inverse, stream)
+                                     : launch_lds_t<uint32_t>(a, p.p, inverse, stream);
         }
         a.groups_per_row = p.W / (p.p * E);
         a.groups = static_cast<uint32_t>(a.numel / (p.p * E));
