@@ -73,7 +73,8 @@ enum {
     LTX3DROPE_REASON_TABLE_DEVICE = 7,   /* the tables live on another device than the tensors */
     LTX3DROPE_REASON_ALIGN = 8,          /* a pointer is not aligned to one pair (2 elements) */
     LTX3DROPE_REASON_OVERLAP = 9,        /* an output overlaps an input or the other output */
-    LTX3DROPE_REASON_TOO_LARGE = 10,     /* B*T*H*W*heads*head_dim >= 2^31 elements */
+    LTX3DROPE_REASON_TOO_LARGE = 10,     /* 3D RoPE: B*T*H*W*heads*head_dim >= 2^32 elements;
+                                            rotate-half RoPE: a tensor of 2^31 elements or more */
     LTX3DROPE_REASON_NOT_DEVICE_PTR = 11,/* a pointer is not device memory of the tables' device */
     LTX3DROPE_REASON_HOST_MODE = 12,     /* the library is in host-table test mode (no launches) */
     LTX3DROPE_REASON_EXTENT = 13         /* a pointer's device allocation ends before the tensor does */
@@ -160,8 +161,9 @@ int ltx3drope_cache_clear(void);
  * pointer or handle; dtype F32 or BF16; B, T, H, W, heads, head_dim > 0;
  * table split widths even and > 0 and summing to head_dim; tables built for
  * (T, H, W); every pointer aligned to one pair (8 B for F32, 4 B for BF16);
- * neither output overlapping an input or the other output; fewer than 2^31
- * elements per tensor; all four pointers device memory of the tables'
+ * neither output overlapping an input or the other output; fewer than 2^32
+ * elements per tensor (8 GiB of bf16, 16 GiB of fp32); all four pointers
+ * device memory of the tables'
  * device, each inside an allocation large enough for the whole tensor
  * (checked last, REASON_NOT_DEVICE_PTR then REASON_EXTENT; skipped in
  * host-table mode).  Pure host logic: no launch, no allocation, no synchronization

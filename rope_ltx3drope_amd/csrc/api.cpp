@@ -203,11 +203,13 @@ int precheck(const void* q_out, const void* k_out, const void* q, const void* k,
     const int nptr = check_outputs ? 4 : 2;
     for (int i = 0; i < nptr; ++i)
         if (reinterpret_cast<uintptr_t>(ptrs[i]) % pair) return LTX3DROPE_REASON_ALIGN;
-    // size limit before any product can overflow: each factor < 2^31 and the running product < 2^31
-    const int64_t lim = int64_t(1) << 31;
+    // Index width: fewer than 2^32 elements per tensor, so the kernels' 32-bit indices hold every
+    // pair (< 2^31) and every 16-byte vector (< 2^30).  Each factor < 2^31 and the running
+    // product < 2^32 are checked before any product can overflow.
+    const int64_t lim = int64_t(1) << 32;
     int64_t numel = 1;
     for (int64_t f : {B, T, H, W, heads, D}) {
-        if (f >= lim || numel > lim / f) return LTX3DROPE_REASON_TOO_LARGE;
+        if (f >= (int64_t(1) << 31) || numel > lim / f) return LTX3DROPE_REASON_TOO_LARGE;
         numel *= f;
     }
     if (numel >= lim) return LTX3DROPE_REASON_TOO_LARGE;
@@ -814,7 +816,8 @@ const char* ltx3drope_reason_string(int reason) {
         case LTX3DROPE_REASON_TABLE_DEVICE: return "tables live on another device";
         case LTX3DROPE_REASON_ALIGN: return "pointers must be aligned to one (even, odd) pair";
         case LTX3DROPE_REASON_OVERLAP: return "outputs must not overlap the inputs or each other";
-        case LTX3DROPE_REASON_TOO_LARGE: return "tensors must have fewer than 2^31 elements";
+        case LTX3DROPE_REASON_TOO_LARGE:
+            return "too many elements (3D RoPE: 2^32 or more per tensor; rotate-half RoPE: 2^31 or more)";
         case LTX3DROPE_REASON_NOT_DEVICE_PTR: return "pointer is not device memory";
         case LTX3DROPE_REASON_HOST_MODE: return "host-table test mode: nothing is launched";
         case LTX3DROPE_REASON_EXTENT: return "a device allocation ends before the tensor does";

@@ -621,16 +621,18 @@ def test_dit_freq_grid_on_device_equals_host():
 
 
 def test_largest_supported_tensor():
-    """15 heads x [1, 16, 64, 1024] x head_dim 128 = 2,013,265,920 elements per tensor, just under the
-    2^31 limit: the gate's full-size verification, fast == plain over the whole output, sampled
-    tokens against the oracle; one more head (2^31 elements) is refused without a launch."""
-    shape, split = (1, 16, 64, 1024, 15, 128), (32, 48, 48)
-    log("largest tensor: generating inputs")
-    q = workloads.generate_bf16_bits(shape, 101)
-    k = workloads.generate_bf16_bits(shape, 102)
-    dq, dk = to_dev(q, oracle.BF16), to_dev(k, oracle.BF16)
+    """31 heads x [1, 16, 64, 1024] x head_dim 128 = 4,160,749,568 elements per tensor (7.75 GiB of
+    bf16), just under the 2^32 limit: the gate's full-size verification, fast == plain over the
+    whole output, sampled tokens (the last included) against the oracle; one more head (2^32
+    elements) is refused without a launch.  Inputs are finite random bf16 patterns drawn on the
+    device."""
+    shape, split = (1, 16, 64, 1024, 31, 128), (32, 48, 48)
+    N, heads, D = 16 * 64 * 1024, 31, 128
+    log("largest tensor: generating inputs on the device")
+    dq = workloads.generate_bf16_bits(shape, 101, DEV)
+    dk = workloads.generate_bf16_bits(shape, 102, DEV)
     with rla.tables_build(16, 64, 1024, split) as tab:
-        too_big = (1, 16, 64, 1024, 16, 128)
+        too_big = (1, 16, 64, 1024, 32, 128)
         reason = ctypes.c_int(0)
         assert _lib.lib().ltx3drope_can_use(None, None, dq.data_ptr(), dk.data_ptr(), _lib.DTYPE_BF16, *too_big,
                                             tab.handle, ctypes.byref(reason)) == 0
@@ -644,7 +646,11 @@ def test_largest_supported_tensor():
         assert torch.equal(qo.view(torch.int16), pq.view(torch.int16))
         assert torch.equal(ko.view(torch.int16), pk.view(torch.int16))
         del pq, pk
-    w = workloads.Workload(0, "largest", oracle.BF16, 1, ((16, 64, 1024),), 15, 128, split, 10000.0, 0, "bits", (0,))
     log("largest tensor: sampled oracle comparison")
-    sampled_check(q, qo, w, 0, 800, seed=90)
-    sampled_check(k, ko, w, 0, 800, seed=91)
+    tabs = oracle.grid_tables(16, 64, 1024, split, 10000.0)
+    for x, out, seed in ((dq, qo, 90), (dk, ko, 91)):
+        ids = workloads.sample_tokens(N, 800, seed)
+        idx = torch.from_numpy(ids).to(DEV)
+        rows = to_host(x.view(N, heads, D)[idx], oracle.BF16)
+        want = oracle.apply_rope_tokens(rows, oracle.BF16, oracle.token_coords(ids, 16, 64, 1024), tabs, split)
+        assert_bitexact(to_host(out.view(N, heads, D)[idx], oracle.BF16), want, oracle.BF16, "sampled tokens")

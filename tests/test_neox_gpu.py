@@ -192,13 +192,10 @@ def test_random_configurations(seed):
 def test_more_tokens_than_the_fast_grid_holds_use_the_plain_kernel():
     """2^25 + 3 tokens of one head of 16 bf16 values: two 64-lane workgroups per token would need
     2^32 work-items or more, so the call runs on the plain kernel; sampled tokens (the last
-    included) against the oracle.  Q and K come from torch's seeded device generator."""
+    included) against the oracle.  Inputs are drawn on the device (workloads.generate_neox_device)."""
     tokens, D, maxp = (1 << 25) + 3, 16, 1000
-    g = torch.Generator(device=DEV).manual_seed(2024)
     log("2^25 + 3 tokens: generating inputs on the device")
-    dq = torch.randn(tokens, 1, D, generator=g, device=DEV).to(torch.bfloat16)
-    dk = torch.randn(tokens, 1, D, generator=g, device=DEV).to(torch.bfloat16)
-    dpos = torch.randint(0, maxp, (tokens,), generator=g, device=DEV, dtype=torch.int64)
+    dq, dk, dpos = workloads.generate_neox_device(tokens, 1, 1, D, maxp, 2024, DEV)
     w = workloads.NeoxWorkload("big", oracle.BF16, 16, 1, 1, D, maxp, oracle.F32, "random", 31)
     _, _, _, cache = workloads.generate_neox(w)
     qo, ko = rla.neox_apply_qk(dq, dk, dpos, to_dev(cache, oracle.F32))

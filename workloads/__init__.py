@@ -135,17 +135,30 @@ def generate(w: Workload, grid_indices: Sequence[int] | None = None) -> List[Tup
     return out
 
 
-def generate_bf16_bits(shape: Sequence[int], seed: int) -> np.ndarray:
-    """Finite bf16 bit patterns of random sign and mantissa with magnitudes in [1/8, 2): a cheap
-    generator for the largest tensors (billions of elements), where normal draws would take minutes."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    n = int(np.prod(shape, dtype=np.int64))
-    out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, _CHUNK * 4):
-        e = min(n, s + _CHUNK * 4)
-        raw = rng.integers(0, 1 << 16, size=e - s, dtype=np.uint16)
-        out[s:e] = (raw & np.uint16(0x81FF)) | np.uint16(0x3E00)  # exponent field 0x7C..0x7F
-    return out.reshape(shape)
+def generate_bf16_bits(shape: Sequence[int], seed: int, device):
+    """Finite bf16 bit patterns of random sign and mantissa with magnitudes in [1/8, 2), drawn with
+    torch's seeded generator on `device` (a torch bf16 tensor): for the largest tensors, billions
+    of elements, which are generated where they are used rather than on the host."""
+    import torch
+
+    g = torch.Generator(device=device).manual_seed(seed)
+    raw = torch.empty(tuple(shape), dtype=torch.int16, device=device).random_(-32768, 32768, generator=g)
+    raw.bitwise_and_(-32257).bitwise_or_(0x3E00)  # keep sign and mantissa (0x81FF); exponent field 0x7C..0x7F
+    return raw.view(torch.bfloat16)
+
+
+def generate_neox_device(tokens: int, q_heads: int, k_heads: int, head_dim: int, max_position: int, seed: int,
+                         device):
+    """Rotate-half RoPE inputs of any size drawn with torch's seeded generator on `device`: q, k
+    bf16 tensors of N(0,1) values (torch's fp32 draw and cast) and int64 positions uniform in
+    [0, max_position).  For token counts whose host generation would take minutes."""
+    import torch
+
+    g = torch.Generator(device=device).manual_seed(seed)
+    q = torch.randn(tokens, q_heads, head_dim, generator=g, device=device).to(torch.bfloat16)
+    k = torch.randn(tokens, k_heads, head_dim, generator=g, device=device).to(torch.bfloat16)
+    pos = torch.randint(0, max_position, (tokens,), generator=g, device=device, dtype=torch.int64)
+    return q, k, pos
 
 
 def generate_custom(shape: Sequence[int], dtype: str, seed: int, scale: float | None = None):
