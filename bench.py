@@ -130,6 +130,8 @@ def parse():
         args.steps = 200 if short else 50
     if args.warmup is None:
         args.warmup = 200 if short else 20
+    if args.steps < 1 or args.warmup < 0 or args.rotate < 0:
+        ap.error("--steps must be at least 1, --warmup and --rotate at least 0")
     return args
 
 

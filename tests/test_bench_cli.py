@@ -39,6 +39,13 @@ def test_defaults_per_op():
     assert (a.steps, a.warmup) == (7, 3)
 
 
+def test_bad_step_counts_are_refused():
+    for argv in (("--steps", "0"), ("--warmup", "-1"), ("--rotate", "-2")):
+        with pytest.raises(SystemExit) as e:
+            parse(*argv)
+        assert e.value.code == 2
+
+
 def test_kernel_source_hash_ignores_comments(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("// a comment\nint x = 1;  // trailing\n/* block\ncomment */\nint y = 2;\n")
