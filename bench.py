@@ -470,13 +470,11 @@ def main_dit(args):
         sys.exit(1)
 
 
-def patch_kernel_name(fast: bool, inverse: bool, p: int, elem_bytes: int) -> str:
-    """The kernel the library picks for a fast-path call (it names none itself)."""
+def patch_kernel_name(fast: bool, inverse: bool) -> str:
+    """The kernel the library picks for a call (it names none itself)."""
     if not fast:
         return "patch_plain"
-    if (16 // elem_bytes) % p == 0:
-        return "unpatch_lds" if inverse else "patch_lds"
-    return "patch_fast"
+    return "unpatch_lds" if inverse else "patch_lds"
 
 
 def main_patch(args):
@@ -556,7 +554,7 @@ def main_patch(args):
                          f"CPU: {_cpu_model()}"}
     mism = int((got != want).sum())
     st = rla.stats()
-    kernel = patch_kernel_name(st["fast_launches"] > 0, inverse, p, eb)
+    kernel = patch_kernel_name(st["fast_launches"] > 0, inverse)
     name = patch_workload_name(args.op, shape, p, eb)
     line = {
         "metric": f"{args.op} (stage-5 space-to-depth) achieved HBM GB/s, bit-exact vs oracle",

@@ -17,23 +17,19 @@
 //  * unpatch_lds<T, P>: the inverse, on 128 unpatched vectors per wavefront in
 //    (b, c, f, height offset, patch row, vector) order: two loads per lane that
 //    each cover whole runs of 128/P packed vectors, two contiguous 1 KB stores.
-//  Both are used whenever a 16-byte vector splits evenly across the P width
-//  offsets (16/sizeof(T) a multiple of p: bf16 with p = 2, 4, 8; fp32 with
-//  p = 2, 4).
-//  * patch_fast<T, P, INVERSE>: one thread per group of P consecutive 16-byte
-//    vectors of an unpatched row, transposed in registers; covers the remaining
-//    fast case (fp32, p = 8), in both directions.
-//  * patch_plain<T, INVERSE>: one element per thread, any shape and element
-//    size (1, 2, 4 or 8 bytes).
-// The fast kernels need W to be a multiple of p * 16/sizeof(T) and 16-byte
-// aligned tensors.
+//  Both take elements of 1, 2, 4 or 8 bytes and p = 2, 4, 8 or 16, 16-byte
+//  aligned tensors and W a multiple of p * 16/sizeof(T).
+//  * patch_plain<T, INVERSE>: one element per thread, any shape, any p and
+//    element size (1, 2, 4 or 8 bytes).
 //
 // Measured on MI355X on a 121-frame 544 x 960 bf16 clip, p = 4 (758 MB moved):
 // threads in unpatched-row order wrote each 480-byte packed row piecemeal
 // (4.1 TB/s); the (b, c, f, height offset, patch row) order with a register
 // transpose reached 5.5 TB/s (patchify) and a per-lane gather 6.0 TB/s
 // (unpatchify); the LDS-staged kernels reach 6.4 (patchify) and 6.5 TB/s
-// (unpatchify) with non-temporal loads and streaming (sc1 | nt) stores.
+// (unpatchify) with non-temporal loads and streaming (sc1 | nt) stores.  (The
+// register transpose, kept for a while for fp32 with p = 8, took 5.4 and
+// 3.3 TB/s there.)
 #include <hip/hip_runtime.h>
 
 #include "fastdiv.h"
@@ -56,8 +52,7 @@ struct PatchArgs {
     const void* src;
     void* dst;
     uint32_t B, C, F, H, W, p;
-    uint32_t groups_per_row;  // fast kernel: W / (P * E)
-    uint32_t groups;          // patch_fast: B*C*F*H*groups_per_row; LDS kernels: 16-byte vectors of the unpatched tensor
+    uint32_t groups;          // LDS kernels: 16-byte vectors of the unpatched tensor
     uint64_t numel;           // plain kernel
     uint32_t dst_bytes;       // LDS kernels: output size in bytes when below 2^31 (streaming stores), else 0
     FastDiv div_WE, div_WpE, div_Hp, div_F;  // LDS kernels: W/E, (W/p)/E, H/p and F (fastdiv.h)
@@ -80,62 +75,6 @@ __device__ __forceinline__ uint64_t packed_offset(const PatchArgs& a, uint32_t b
     const uint32_t Hp = a.H / a.p, Wp = a.W / a.p;
     const uint64_t co = (static_cast<uint64_t>(b) * a.C + c) * a.p * a.p + static_cast<uint64_t>(pw) * a.p + ph;
     return ((co * a.F + f) * Hp + hh) * Wp + ww;
-}
-
-template <typename T, int P, bool INVERSE>
-__global__ void __launch_bounds__(kBlock) patch_fast(PatchArgs a) {
-    constexpr int E = 16 / sizeof(T);
-    const uint32_t g = blockIdx.x * kBlock + threadIdx.x;
-    if (g >= a.groups) return;
-    // thread order (b, c, f, ph, hh, gi): consecutive threads walk the patch rows of one
-    // height offset, so a wavefront's stores for one width offset fill consecutive rows of
-    // one output plane, and each input row is read whole by one wavefront
-    uint32_t t = g / a.groups_per_row;
-    const uint32_t gi = g - t * a.groups_per_row;
-    const uint32_t Hp = a.H / P;
-    const uint32_t hh = t % Hp;
-    t /= Hp;
-    const uint32_t ph = t % P;
-    t /= P;
-    const uint32_t f = t % a.F;
-    t /= a.F;
-    const uint32_t c = t % a.C;
-    const uint32_t b = t / a.C;
-    const uint64_t row = ((static_cast<uint64_t>(b) * a.C + c) * a.F + f) * a.H + hh * P + ph;
-    const uint64_t row_off = row * a.W + static_cast<uint64_t>(gi) * (P * E);
-    const T* src = static_cast<const T*>(a.src);
-    T* dst = static_cast<T*>(a.dst);
-    if constexpr (!INVERSE) {
-        Vec<T> in[P];
-#pragma unroll
-        for (int r = 0; r < P; ++r)
-            in[r] = __builtin_bit_cast(Vec<T>, reinterpret_cast<const u32x4*>(src + row_off)[r]);
-#pragma unroll
-        for (int pw = 0; pw < P; ++pw) {
-            Vec<T> o;
-#pragma unroll
-            for (int w = 0; w < E; ++w) o.e[w] = in[(w * P + pw) / E].e[(w * P + pw) % E];
-            const uint64_t off = packed_offset(a, b, c, pw, ph, f, hh, gi * E);
-            *reinterpret_cast<u32x4*>(dst + off) = __builtin_bit_cast(u32x4, o);
-        }
-    } else {
-        Vec<T> in[P];
-#pragma unroll
-        for (int pw = 0; pw < P; ++pw) {
-            const uint64_t off = packed_offset(a, b, c, pw, ph, f, hh, gi * E);
-            in[pw] = __builtin_bit_cast(Vec<T>, *reinterpret_cast<const u32x4*>(src + off));
-        }
-#pragma unroll
-        for (int r = 0; r < P; ++r) {
-            Vec<T> o;
-#pragma unroll
-            for (int j = 0; j < E; ++j) {
-                const int col = r * E + j;  // column inside the group: w * P + pw
-                o.e[j] = in[col % P].e[col / P];
-            }
-            reinterpret_cast<u32x4*>(dst + row_off)[r] = __builtin_bit_cast(u32x4, o);
-        }
-    }
 }
 
 // (b*C + c, f, height offset, patch row) of row `rowid`.  PH_OUTER: rows in (b, c, height
@@ -193,11 +132,69 @@ __device__ __forceinline__ uint64_t packed_offset0(const PatchArgs& a, uint32_t 
 template <int NB>
 struct Chunk;
 template <>
+struct Chunk<1> { typedef uint8_t type; };
+template <>
 struct Chunk<2> { typedef uint16_t type; };
 template <>
 struct Chunk<4> { typedef uint32_t type; };
 template <>
 struct Chunk<8> { typedef unsigned type __attribute__((ext_vector_type(2))); };
+
+// Regrouping through LDS.  Element g of a run of unpatched elements that starts on a multiple of P
+// belongs to width-offset plane g % P, at element g / P of that plane's run (rows hold a whole
+// number of P-element groups).  For local 16-byte vector li, elements li*E .. li*E + E - 1:
+//  * E a multiple of P: each plane gets K = E/P consecutive elements, one K-element chunk at
+//    position li*K of lds[pw];
+//  * P a multiple of E: R = P/E consecutive vectors share a position, and element e goes to its
+//    own plane (li % R)*E + e, at position li / R.
+template <typename T, int P, int N>
+__device__ __forceinline__ void scatter_vector(T (&lds)[P][N], uint32_t li, const Vec<T>& v) {
+    constexpr int E = 16 / sizeof(T);
+    if constexpr (E % P == 0) {
+        constexpr int K = E / P;
+        typedef typename Chunk<K * sizeof(T)>::type Ch;
+#pragma unroll
+        for (int pw = 0; pw < P; ++pw) {
+            T ch[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) ch[k] = v.e[k * P + pw];
+            Ch c;
+            __builtin_memcpy(&c, ch, sizeof(Ch));
+            reinterpret_cast<Ch*>(&lds[pw][0])[li] = c;
+        }
+    } else {
+        static_assert(P % E == 0, "P and the vector's element count must divide one another");
+        constexpr uint32_t R = P / E;
+        const uint32_t pos = li / R, pw0 = (li % R) * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) lds[pw0 + e][pos] = v.e[e];
+    }
+}
+
+template <typename T, int P, int N>
+__device__ __forceinline__ Vec<T> gather_vector(const T (&lds)[P][N], uint32_t li) {
+    constexpr int E = 16 / sizeof(T);
+    Vec<T> v;
+    if constexpr (E % P == 0) {
+        constexpr int K = E / P;
+        typedef typename Chunk<K * sizeof(T)>::type Ch;
+#pragma unroll
+        for (int pw = 0; pw < P; ++pw) {
+            const Ch c = reinterpret_cast<const Ch*>(&lds[pw][0])[li];
+            T ch[K];
+            __builtin_memcpy(ch, &c, sizeof(Ch));
+#pragma unroll
+            for (int k = 0; k < K; ++k) v.e[k * P + pw] = ch[k];
+        }
+    } else {
+        static_assert(P % E == 0, "P and the vector's element count must divide one another");
+        constexpr uint32_t R = P / E;
+        const uint32_t pos = li / R, pw0 = (li % R) * E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) v.e[e] = lds[pw0 + e][pos];
+    }
+    return v;
+}
 
 // A workgroup of P wavefronts owns unpatched vectors [w*P*64, (w+1)*P*64) and packed vectors
 // [w*64, (w+1)*64) of every width-offset plane.  Thread t loads unpatched vector w*P*64 + t,
@@ -209,10 +206,7 @@ struct Chunk<8> { typedef unsigned type __attribute__((ext_vector_type(2))); };
 template <typename T, int P>
 __global__ void __launch_bounds__(P * kBlock) patch_lds(PatchArgs a) {
     constexpr int E = 16 / sizeof(T);
-    constexpr int K = E / P;
-    static_assert(K * P == E, "a vector must split evenly across the width offsets");
     constexpr uint32_t U = P * kBlock;  // unpatched vectors per workgroup
-    typedef typename Chunk<K * sizeof(T)>::type Ch;
     __shared__ __align__(16) T lds[P][kBlock * E];
     const uint32_t t = threadIdx.x;
     const uint32_t first = blockIdx.x * U;
@@ -220,17 +214,8 @@ __global__ void __launch_bounds__(P * kBlock) patch_lds(PatchArgs a) {
     const uint32_t valid = left < U ? left : U;  // a multiple of P: rows are whole groups of P vectors
     if (t < valid) {
         const T* src = static_cast<const T*>(a.src);
-        const Vec<T> v = __builtin_bit_cast(
-            Vec<T>, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + unpatched_offset<P, E, true>(a, first + t))));
-#pragma unroll
-        for (int pw = 0; pw < P; ++pw) {
-            T ch[K];
-#pragma unroll
-            for (int k = 0; k < K; ++k) ch[k] = v.e[k * P + pw];
-            Ch c;
-            __builtin_memcpy(&c, ch, sizeof(Ch));
-            reinterpret_cast<Ch*>(&lds[pw][0])[t] = c;
-        }
+        scatter_vector<T, P>(lds, t, __builtin_bit_cast(Vec<T>, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                                              src + unpatched_offset<P, E, true>(a, first + t)))));
     }
     __syncthreads();
     const uint32_t pw = t / kBlock, j = t % kBlock;  // wavefront pw stores plane pw
@@ -252,11 +237,8 @@ constexpr uint32_t kUnpatchVectors = 2 * kBlock;  // unpatched 16-byte vectors p
 template <typename T, int P>
 __global__ void __launch_bounds__(kBlock) unpatch_lds(PatchArgs a) {
     constexpr int E = 16 / sizeof(T);
-    constexpr int K = E / P;
-    static_assert(K * P == E, "a vector must split evenly across the width offsets");
     constexpr uint32_t U = kUnpatchVectors;
     constexpr uint32_t PV = U / P;  // packed vectors of each plane per wavefront
-    typedef typename Chunk<K * sizeof(T)>::type Ch;
     __shared__ __align__(16) T lds[P][PV * E];
     const uint32_t lane = threadIdx.x;
     const uint32_t first = blockIdx.x * U;
@@ -279,16 +261,8 @@ __global__ void __launch_bounds__(kBlock) unpatch_lds(PatchArgs a) {
     for (uint32_t r = 0; r < U / kBlock; ++r) {
         const uint32_t li = r * kBlock + lane;
         if (li >= valid) break;
-        Vec<T> v;
-#pragma unroll
-        for (int pw = 0; pw < P; ++pw) {
-            const Ch c = reinterpret_cast<const Ch*>(&lds[pw][0])[li];
-            T ch[K];
-            __builtin_memcpy(ch, &c, sizeof(Ch));
-#pragma unroll
-            for (int k = 0; k < K; ++k) v.e[k * P + pw] = ch[k];
-        }
-        store_out<T>(a, unpatched_offset<P, E, false>(a, first + li), __builtin_bit_cast(u32x4, v));
+        store_out<T>(a, unpatched_offset<P, E, false>(a, first + li),
+                     __builtin_bit_cast(u32x4, gather_vector<T, P>(lds, li)));
     }
 }
 
@@ -317,18 +291,6 @@ __global__ void __launch_bounds__(256) patch_plain(PatchArgs a) {
     }
 }
 
-template <typename T, bool INV>
-hipError_t launch_fast_t(PatchArgs a, uint32_t P, hipStream_t stream) {
-    const uint32_t blocks = (a.groups + kBlock - 1) / kBlock;
-    switch (P) {
-        case 2: hipLaunchKernelGGL((patch_fast<T, 2, INV>), dim3(blocks), dim3(kBlock), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((patch_fast<T, 4, INV>), dim3(blocks), dim3(kBlock), 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((patch_fast<T, 8, INV>), dim3(blocks), dim3(kBlock), 0, stream, a); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
 template <bool INV>
 hipError_t launch_plain_t(PatchArgs a, uint32_t elem_bytes, hipStream_t stream, int cu_count) {
     const uint64_t want = (a.numel + 255) / 256;
@@ -344,41 +306,39 @@ hipError_t launch_plain_t(PatchArgs a, uint32_t elem_bytes, hipStream_t stream, 
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_lds_t(PatchArgs a, uint32_t P, bool inverse, hipStream_t stream) {
-    constexpr uint32_t E = 16 / sizeof(T);
+template <typename T, int P>
+hipError_t launch_lds_tp(const PatchArgs& a, bool inverse, hipStream_t stream) {
     const uint32_t per_block = inverse ? kUnpatchVectors : P * kBlock;  // unpatched vectors per workgroup
     const uint32_t blocks = (a.groups + per_block - 1) / per_block;
-    const uint32_t threads = inverse ? kBlock : P * kBlock;
+    if (inverse)
+        hipLaunchKernelGGL((unpatch_lds<T, P>), dim3(blocks), dim3(kBlock), 0, stream, a);
+    else
+        hipLaunchKernelGGL((patch_lds<T, P>), dim3(blocks), dim3(P * kBlock), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_lds_t(const PatchArgs& a, uint32_t P, bool inverse, hipStream_t stream) {
     switch (P) {
-        case 2:
-            if (inverse) hipLaunchKernelGGL((unpatch_lds<T, 2>), dim3(blocks), dim3(threads), 0, stream, a);
-            else hipLaunchKernelGGL((patch_lds<T, 2>), dim3(blocks), dim3(threads), 0, stream, a);
-            break;
-        case 4:
-            if (inverse) hipLaunchKernelGGL((unpatch_lds<T, 4>), dim3(blocks), dim3(threads), 0, stream, a);
-            else hipLaunchKernelGGL((patch_lds<T, 4>), dim3(blocks), dim3(threads), 0, stream, a);
-            break;
-        case 8:
-            if constexpr (E % 8 == 0) {
-                if (inverse) hipLaunchKernelGGL((unpatch_lds<T, 8>), dim3(blocks), dim3(threads), 0, stream, a);
-                else hipLaunchKernelGGL((patch_lds<T, 8>), dim3(blocks), dim3(threads), 0, stream, a);
-                break;
-            }
-            return hipErrorInvalidValue;
+        case 2: return launch_lds_tp<T, 2>(a, inverse, stream);
+        case 4: return launch_lds_tp<T, 4>(a, inverse, stream);
+        case 8: return launch_lds_tp<T, 8>(a, inverse, stream);
+        case 16: return launch_lds_tp<T, 16>(a, inverse, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace
 
+// The LDS kernels: 1, 2, 4 or 8-byte elements, p = 2, 4, 8 or 16 (so p and the 16/elem_bytes
+// elements of a vector divide one another), 16-byte aligned tensors and W a multiple of
+// p * 16/elem_bytes (then W/p is a multiple of 16/elem_bytes too: packed vectors stay aligned).
 bool patch_fast_supported(const PatchProblem& p) {
-    if (p.elem_bytes != 2 && p.elem_bytes != 4) return false;
-    if (p.p != 2 && p.p != 4 && p.p != 8) return false;
+    if (p.elem_bytes != 1 && p.elem_bytes != 2 && p.elem_bytes != 4 && p.elem_bytes != 8) return false;
+    if (p.p != 2 && p.p != 4 && p.p != 8 && p.p != 16) return false;
     if (reinterpret_cast<uintptr_t>(p.src) % 16 || reinterpret_cast<uintptr_t>(p.dst) % 16) return false;
     const uint32_t E = 16 / p.elem_bytes;
-    return p.W % (p.p * E) == 0;  // then W/p is a multiple of E too: output vectors stay aligned
+    return p.W % (p.p * E) == 0;
 }
 
 hipError_t launch_patch(const PatchProblem& p, bool inverse, hipStream_t stream, int cu_count) {
@@ -392,27 +352,23 @@ hipError_t launch_patch(const PatchProblem& p, bool inverse, hipStream_t stream,
     a.W = p.W;
     a.p = p.p;
     a.numel = static_cast<uint64_t>(p.B) * p.C * p.F * p.H * p.W;
-    a.groups_per_row = 0;
     a.groups = 0;
-    const uint64_t bytes = static_cast<uint64_t>(p.B) * p.C * p.F * p.H * p.W * p.elem_bytes;
+    const uint64_t bytes = a.numel * p.elem_bytes;
     a.dst_bytes = bytes < (uint64_t(1) << 31) ? static_cast<uint32_t>(bytes) : 0u;
     if (a.numel == 0) return hipSuccess;
     if (patch_fast_supported(p) && !p.force_plain) {
         const uint32_t E = 16 / p.elem_bytes;
-        if (E % p.p == 0) {
-            a.groups = static_cast<uint32_t>(a.numel / E);  // 16-byte vectors of the unpatched tensor
-            a.div_WE = make_fastdiv(p.W / E);
-            a.div_WpE = make_fastdiv(p.W / p.p / E);
-            a.div_Hp = make_fastdiv(p.H / p.p);
-            a.div_F = make_fastdiv(p.F);
-            return p.elem_bytes == 2 ? launch_lds_t<uint16_t>(a, p.p, inverse, stream)
-                                     : launch_lds_t<uint32_t>(a, p.p, inverse, stream);
+        a.groups = static_cast<uint32_t>(a.numel / E);  // 16-byte vectors of the unpatched tensor
+        a.div_WE = make_fastdiv(p.W / E);
+        a.div_WpE = make_fastdiv(p.W / p.p / E);
+        a.div_Hp = make_fastdiv(p.H / p.p);
+        a.div_F = make_fastdiv(p.F);
+        switch (p.elem_bytes) {
+            case 1: return launch_lds_t<uint8_t>(a, p.p, inverse, stream);
+            case 2: return launch_lds_t<uint16_t>(a, p.p, inverse, stream);
+            case 4: return launch_lds_t<uint32_t>(a, p.p, inverse, stream);
+            default: return launch_lds_t<uint64_t>(a, p.p, inverse, stream);
         }
-        a.groups_per_row = p.W / (p.p * E);
-        a.groups = static_cast<uint32_t>(a.numel / (p.p * E));
-        if (p.elem_bytes == 2)
-            return inverse ? launch_fast_t<uint16_t, true>(a, p.p, stream) : launch_fast_t<uint16_t, false>(a, p.p, stream);
-        return inverse ? launch_fast_t<uint32_t, true>(a, p.p, stream) : launch_fast_t<uint32_t, false>(a, p.p, stream);
     }
     return inverse ? launch_plain_t<true>(a, p.elem_bytes, stream, cu_count)
                    : launch_plain_t<false>(a, p.elem_bytes, stream, cu_count);

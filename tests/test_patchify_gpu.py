@@ -37,13 +37,15 @@ def to_host(t, like):
     return t.cpu().numpy().view(like.dtype)
 
 
-@pytest.mark.parametrize("key", ["p1", "p2", "p3", "p4", "p5", "p7", "p8", "p9", "p10", "p11"])
+@pytest.mark.parametrize("key", ["p1", "p2", "p3", "p4", "p5", "p7", "p8", "p9", "p10", "p11", "p13", "p14", "p15",
+                                 "p16", "p17", "p18", "p19", "p20", "p21"])
 @pytest.mark.parametrize("path", [0, 2], ids=["fast", "plain"])
 def test_patchify_and_inverse_full(key, path):
     shape, p, eb = workloads.PATCH_WORKLOADS[key]
     x = workloads.generate_patch(shape, eb, seed=len(key) + p)
     rla.set_option(rla.OPT_PATH, path)
-    fast = path == 0 and shape[4] % (p * 16 // eb) == 0  # the library's rule for its fast kernels
+    # the library's rule for its fast kernels
+    fast = path == 0 and p in (2, 4, 8, 16) and shape[4] % (p * 16 // eb) == 0
     y = rla.patchify(to_dev(x), p)
     torch.cuda.synchronize()
     want = pf.patchify(x, p)
@@ -57,8 +59,8 @@ def test_patchify_and_inverse_full(key, path):
     assert (st["fast_launches"], st["plain_launches"]) == ((3, 0) if fast else (0, 3))
 
 
-@pytest.mark.parametrize("eb", [1, 8])
-def test_other_element_sizes_use_the_plain_kernel(eb):
+@pytest.mark.parametrize("eb", [1, 2, 4, 8])
+def test_patch_sizes_other_than_2_4_8_16_use_the_plain_kernel(eb):
     shape, p = (2, 3, 2, 12, 18), 3
     x = workloads.generate_patch(shape, eb, seed=eb)
     y = rla.patchify(to_dev(x), p)
@@ -105,9 +107,7 @@ def test_output_of_2_gib_or_more():
     shape, p = (1, 8, 129, 1088, 960), 4
     B, C, F, H, W = shape
     assert B * C * F * H * W * 2 >= 2 ** 31 and B * C * F * H * W < 2 ** 31
-    g = torch.Generator(device=DEV)
-    g.manual_seed(123)
-    x = torch.randint(-32768, 32767, shape, dtype=torch.int16, device=DEV, generator=g)
+    x = workloads.generate_patch_device(shape, 2, 123, DEV)
     y = rla.patchify(x, p)
     rla.set_option(rla.OPT_PATH, 2)
     y_plain = rla.patchify(x, p)

@@ -258,7 +258,31 @@ PATCH_WORKLOADS = {
     "p9": ((1, 2, 3, 16, 64), 8, 4),         # fp32, p = 8: a vector does not split across 8 offsets
     "p10": ((1, 1, 3, 24, 192), 8, 2),       # bf16, p = 8, last wavefront partly filled
     "p11": ((1, 5, 1, 4, 64), 4, 2),         # bf16, p = 4, one partly filled wavefront
+    "p12": ((1, 3, 121, 544, 960), 8, 4),    # the 121-frame clip in fp32 with p = 8
+    # element sizes and patch sizes where a vector's elements and p divide one another either way
+    "p13": ((1, 3, 3, 6, 64), 2, 1),          # u8, p = 2
+    "p14": ((1, 1, 5, 4, 128), 4, 1),         # u8, p = 4, one partly filled workgroup
+    "p15": ((1, 3, 2, 32, 256), 16, 1),       # u8, p = 16: 16-wavefront workgroups
+    "p16": ((1, 1, 2, 32, 256), 16, 2),       # bf16, p = 16
+    "p17": ((1, 3, 5, 16, 96), 8, 4),         # fp32, p = 8: each element to its own plane
+    "p18": ((1, 1, 2, 32, 128), 16, 4),       # fp32, p = 16
+    "p19": ((1, 3, 3, 6, 20), 2, 8),          # 8-byte elements, p = 2
+    "p20": ((2, 3, 3, 16, 48), 8, 8),         # 8-byte elements, p = 8, partly filled
+    "p21": ((1, 3, 3, 16, 64), 16, 8),        # 8-byte elements, p = 16
 }
+
+
+def generate_patch_device(shape, elem_bytes: int, seed: int, device):
+    """Random bit patterns of the element width drawn with torch's seeded generator on `device`
+    (a torch integer tensor of that width), for tensors too large to draw on the host quickly."""
+    import torch
+
+    dt = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[elem_bytes]
+    g = torch.Generator(device=device).manual_seed(seed)
+    lo, hi = (0, 256) if elem_bytes == 1 else (-(1 << (8 * elem_bytes - 1)), 1 << (8 * elem_bytes - 1))
+    if elem_bytes == 8:
+        lo, hi = -(1 << 62), 1 << 62  # random_ wants both bounds representable
+    return torch.empty(tuple(shape), dtype=dt, device=device).random_(lo, hi, generator=g)
 
 
 def generate_patch(shape, elem_bytes: int, seed: int) -> np.ndarray:
