@@ -283,8 +283,9 @@ int ltx3drope_neox_position_errors(int device, int reset, int64_t* count);
  * contiguous, elements of elem_bytes = 1, 2, 4 or 8 bytes (the op moves data
  * and never looks at values, so it is exact for every dtype).  B, C, F, H, W
  * are always the unpatched sizes.  E_INVALID: a size or p <= 0, H or W not a
- * multiple of p, elem_bytes not 1/2/4/8, NULL pointers.  E_UNSUPPORTED: 2^31
- * elements or more, pointers not aligned to one element, overlapping tensors,
+ * multiple of p, elem_bytes not 1/2/4/8, NULL pointers.  E_UNSUPPORTED: 2^32
+ * elements or more (or C*p*p of 2^31 or more), pointers not aligned to one
+ * element, overlapping tensors,
  * not device memory of one device, or allocations smaller than the tensors.
  * Asynchronous on `stream`.  E_NOMEM / E_HIP: the device's first call could not
  * allocate the library's 256-byte per-device counter block; E_HIP: a failed

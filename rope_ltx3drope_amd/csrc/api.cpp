@@ -636,16 +636,18 @@ int patch_call(void* dst, const void* src, int elem_bytes, int64_t B, int64_t C,
     if (!dst || !src) return LTX3DROPE_E_INVALID;
     if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return LTX3DROPE_E_INVALID;
     if (B <= 0 || C <= 0 || F <= 0 || H <= 0 || W <= 0 || p <= 0 || H % p || W % p) return LTX3DROPE_E_INVALID;
-    const int64_t lim = int64_t(1) << 31;
+    // fewer than 2^32 elements (the LDS kernels index 16-byte vectors with 32 bits), each size and
+    // the packed channel count C*p*p below 2^31
+    const int64_t lim = int64_t(1) << 32, size_lim = int64_t(1) << 31;
     int64_t numel = 1;
     for (int64_t f : {B, C, F, H, W}) {
-        if (f >= lim || numel > lim / f) {
+        if (f >= size_lim || numel > lim / f) {
             stats().rejected.fetch_add(1);
             return LTX3DROPE_E_UNSUPPORTED;
         }
         numel *= f;
     }
-    if (numel >= lim || p * p > lim / C) {
+    if (numel >= lim || p >= size_lim || p * p > size_lim / C) {
         stats().rejected.fetch_add(1);
         return LTX3DROPE_E_UNSUPPORTED;
     }

@@ -127,3 +127,32 @@ def test_output_of_2_gib_or_more():
         np.testing.assert_array_equal(got, want)
     st = rla.stats()
     assert st["fast_launches"] == 2 and st["plain_launches"] == 1
+
+
+def test_4k_clip_of_more_than_2_to_the_31_elements():
+    """A 121-frame 2160 x 3840 RGB clip in bf16 with p = 4: 3,010,560,000 elements (between 2^31 and
+    2^32, 6 GB per tensor), drawn on the device.  The LDS kernels against the plain kernel over the
+    whole output, the round trip, and sampled frames against the oracle."""
+    shape, p = (1, 3, 121, 2160, 3840), 4
+    B, C, F, H, W = shape
+    assert 2 ** 31 < B * C * F * H * W < 2 ** 32
+    x = workloads.generate_patch_device(shape, 2, 4096, DEV)
+    y = rla.patchify(x, p)
+    rla.set_option(rla.OPT_PATH, 2)
+    y_plain = rla.patchify(x, p)
+    rla.set_option(rla.OPT_PATH, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_plain)
+    del y_plain
+    back = rla.unpatchify(y, p)
+    torch.cuda.synchronize()
+    assert torch.equal(back, x)
+    del back
+    rng = np.random.default_rng(9)
+    for c, f in zip(rng.integers(0, C, 4), [0, F - 1, *rng.integers(0, F, 2)]):
+        frame = x[0:1, c:c + 1, f:f + 1].cpu().numpy()
+        want = pf.patchify(frame, p)[0, :, 0]
+        got = y[0, c * p * p:(c + 1) * p * p, f].cpu().numpy()
+        np.testing.assert_array_equal(got, want)
+    st = rla.stats()
+    assert st["fast_launches"] == 2 and st["plain_launches"] == 1
