@@ -142,6 +142,7 @@ RAGGED = [
     ((1, 2, 2, 3, 4, 256), (86, 86, 84), oracle.BF16),    # 128 pairs: two per lane
     ((2, 2, 1, 3, 2, 1024), (342, 342, 340), oracle.BF16),  # the largest row the LDS holds (4 KB)
     ((1, 1, 2, 2, 32, 1040), (346, 348, 346), oracle.BF16),  # larger: per-pair table loads
+    ((1, 1, 2, 2, 16, 1056), (352, 352, 352), oracle.BF16),  # larger, whole vectors: direct 16-byte loads
 ]
 
 
