@@ -105,6 +105,9 @@ def parse():
     ap.add_argument("--grid", type=int, default=0, help="grid index inside the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-threads", type=int, default=None,
+                    help="rope3d: threads of the additional all-cores oracle run (default: the usable cores, "
+                         "at most 16; 0 or 1 skips it)")
     ap.add_argument("--op", choices=("rope3d", "neox", "patchify", "unpatchify", "dit_freqs"), default="rope3d",
                     help="rope3d: the fused 3D RoPE (default); neox: the rotate-half RoPE with a gathered cache; "
                          "patchify / unpatchify: the stage-5 space-to-depth and its inverse")
@@ -130,6 +133,11 @@ def parse():
         args.steps = 200 if short else 50
     if args.warmup is None:
         args.warmup = 200 if short else 20
+    if args.cpu_threads is None:
+        try:
+            args.cpu_threads = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            args.cpu_threads = min(16, os.cpu_count() or 1)
     if args.steps < 1 or args.warmup < 0 or args.rotate < 0:
         ap.error("--steps must be at least 1, --warmup and --rotate at least 0")
     return args
@@ -301,7 +309,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, gi, q_np, k_np, args.cpu_seconds)
+        cpu = cpu_baseline(w, gi, q_np, k_np, args.cpu_seconds, args.cpu_threads)
 
     traffic = measured_traffic(w.name)
     line = {
@@ -633,37 +641,64 @@ def neox_cpu_baseline(w, q_np, k_np, pos_np, cache_np, target_s):
                       f"{chunk}-token chunks, Q and K; numpy, one thread pinned to one core; CPU: {_cpu_model()}"}
 
 
-def cpu_baseline(w, gi, q_np, k_np, target_s):
+def cpu_baseline(w, gi, q_np, k_np, target_s, threads=0):
     """The oracle, untuned, on whole (batch, frame) slabs of the same inputs (Q and K), single thread,
-    until about target_s seconds of CPU work are done."""
+    until about target_s seconds of CPU work are done.  With threads > 1, also the same oracle on
+    every slab from a pool of that many threads (numpy releases the interpreter lock inside its
+    array operations), whole passes over the workload for about target_s / 2 seconds, under
+    "all_cores"."""
     import numpy as np
 
     import oracle
 
-    pin_one_core()
     B, T, H, W, heads, D = w.shape(gi)
     t0 = time.perf_counter()
     tabs = oracle.grid_tables(T, H, W, w.split, w.base)
     t_tab = time.perf_counter() - t0
     per_slab = 2 * H * W * heads * D
+
+    def slab(i):
+        b, t = divmod(i, T)
+        for x in (q_np, k_np):
+            oracle.rope3d(np.ascontiguousarray(x[b:b + 1, t:t + 1]), w.dtype, w.split, w.base,
+                          tables=_slice_tables(tabs, t))
+        return per_slab
+
+    all_cores = None
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        done, passes = 0, 0
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            while True:
+                done += sum(ex.map(slab, range(B * T)))
+                passes += 1
+                if time.perf_counter() - t0 >= target_s / 2:
+                    break
+        dt = time.perf_counter() - t0
+        all_cores = {"value": round(done / dt * 2 * w.itemsize / 1e9, 4), "unit": "GB/s", "cores": threads,
+                     "gelem_per_s": round(done / dt / 1e9, 5), "seconds": round(dt, 2),
+                     "sample": f"{passes} whole pass(es) over the {B * T} (batch, frame) slabs, Q and K, tables "
+                               f"prebuilt; {threads} threads"}
+    pin_one_core()
     done = 0
     slabs = 0
     t0 = time.perf_counter()
     while slabs < B * T:
-        b, t = divmod(slabs, T)
-        for x in (q_np, k_np):
-            oracle.rope3d(np.ascontiguousarray(x[b:b + 1, t:t + 1]), w.dtype, w.split, w.base,
-                          tables=_slice_tables(tabs, t))
-        done += per_slab
+        done += slab(slabs)
         slabs += 1
         if time.perf_counter() - t0 >= target_s:
             break
     dt = time.perf_counter() - t0 + t_tab
     eps = done / dt
-    return {"value": round(eps * 2 * w.itemsize / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "gelem_per_s": round(eps / 1e9, 5), "seconds": round(dt, 2),
-            "sample": f"{slabs} of {B * T} (batch, frame) slabs, Q and K ({done} elements), plus the grid's "
-                      f"table build; numpy, one thread pinned to one core; CPU: {_cpu_model()}"}
+    out = {"value": round(eps * 2 * w.itemsize / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "gelem_per_s": round(eps / 1e9, 5), "seconds": round(dt, 2),
+           "sample": f"{slabs} of {B * T} (batch, frame) slabs, Q and K ({done} elements), plus the grid's "
+                     f"table build; numpy, one thread pinned to one core; CPU: {_cpu_model()}"}
+    if all_cores is not None:
+        out["all_cores"] = all_cores
+    return out
 
 
 def _slice_tables(tabs, t):
