@@ -73,8 +73,7 @@ enum {
     LTX3DROPE_REASON_TABLE_DEVICE = 7,   /* the tables live on another device than the tensors */
     LTX3DROPE_REASON_ALIGN = 8,          /* a pointer is not aligned to one pair (2 elements) */
     LTX3DROPE_REASON_OVERLAP = 9,        /* an output overlaps an input or the other output */
-    LTX3DROPE_REASON_TOO_LARGE = 10,     /* 3D RoPE: B*T*H*W*heads*head_dim >= 2^32 elements;
-                                            rotate-half RoPE: a tensor of 2^31 elements or more */
+    LTX3DROPE_REASON_TOO_LARGE = 10,     /* a tensor of 2^32 elements or more */
     LTX3DROPE_REASON_NOT_DEVICE_PTR = 11,/* a pointer is not device memory of the tables' device */
     LTX3DROPE_REASON_HOST_MODE = 12,     /* the library is in host-table test mode (no launches) */
     LTX3DROPE_REASON_EXTENT = 13         /* a pointer's device allocation ends before the tensor does */
@@ -256,7 +255,8 @@ int ltx3drope_apply_qk_shard(void* q_out, void* k_out, const void* q, const void
  * ltx3drope_neox_position_errors).  One launch for Q and K, on `stream`.
  * Reasons: NULLPTR, DTYPE (q or cache dtype), NONPOSITIVE_DIM, SPLIT_ODD
  * (odd head_dim), ALIGN (element alignment; positions 8 B), OVERLAP,
- * TOO_LARGE (a tensor of 2^31 elements or more), NOT_DEVICE_PTR,
+ * TOO_LARGE (a tensor or the cache of 2^32 elements or more, or a size of
+ * 2^31 or more), NOT_DEVICE_PTR,
  * TABLE_DEVICE (pointers on different devices), EXTENT.  apply_qk returns
  * E_UNSUPPORTED for any of these; the first call on a device allocates the
  * device's 256-byte counter (E_NOMEM when out of memory, E_HIP for another

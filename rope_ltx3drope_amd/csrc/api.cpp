@@ -402,11 +402,12 @@ int neox_precheck(const void* q_out, const void* k_out, const void* q, const voi
         if (reinterpret_cast<uintptr_t>(p) % es) return LTX3DROPE_REASON_ALIGN;
     if (reinterpret_cast<uintptr_t>(cache) % cs || reinterpret_cast<uintptr_t>(positions) % 8)
         return LTX3DROPE_REASON_ALIGN;
-    const int64_t lim = int64_t(1) << 31;
+    // fewer than 2^32 elements per tensor (and per cache), each size below 2^31
+    const int64_t lim = int64_t(1) << 32, size_lim = int64_t(1) << 31;
     auto product_ok = [&](std::initializer_list<int64_t> fs) {
         int64_t n = 1;
         for (int64_t f : fs) {
-            if (f >= lim || n > lim / f) return false;
+            if (f >= size_lim || n > lim / f) return false;
             n *= f;
         }
         return n < lim;
@@ -818,8 +819,7 @@ const char* ltx3drope_reason_string(int reason) {
         case LTX3DROPE_REASON_TABLE_DEVICE: return "tables live on another device";
         case LTX3DROPE_REASON_ALIGN: return "pointers must be aligned to one (even, odd) pair";
         case LTX3DROPE_REASON_OVERLAP: return "outputs must not overlap the inputs or each other";
-        case LTX3DROPE_REASON_TOO_LARGE:
-            return "too many elements (3D RoPE: 2^32 or more per tensor; rotate-half RoPE: 2^31 or more)";
+        case LTX3DROPE_REASON_TOO_LARGE: return "tensors must have fewer than 2^32 elements";
         case LTX3DROPE_REASON_NOT_DEVICE_PTR: return "pointer is not device memory";
         case LTX3DROPE_REASON_HOST_MODE: return "host-table test mode: nothing is launched";
         case LTX3DROPE_REASON_EXTENT: return "a device allocation ends before the tensor does";

@@ -200,11 +200,11 @@ __global__ void __launch_bounds__(kBlock) neox_fast(NeoxArgs a) {
 template <bool QBF16, bool CBF16>
 __global__ void __launch_bounds__(256) neox_plain(NeoxArgs a) {
     const uint32_t half = a.D / 2;
-    const uint32_t total = a.q_items + a.k_items;  // element pairs of Q, then of K
+    const uint64_t total = uint64_t(a.q_items) + a.k_items;  // element pairs of Q, then of K
     const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t g = blockIdx.x * blockDim.x + threadIdx.x; g < total; g += stride) {
+    for (uint64_t g = blockIdx.x * blockDim.x + threadIdx.x; g < total; g += stride) {
         const bool second = g >= a.q_items;
-        const uint32_t i = second ? g - a.q_items : g;
+        const uint32_t i = static_cast<uint32_t>(second ? g - a.q_items : g);
         const uint32_t heads = second ? a.k_heads : a.q_heads;
         const uint32_t col = i % half;
         const uint32_t row = i / half;  // (token, head)
@@ -317,10 +317,10 @@ hipError_t launch_neox_fast(const NeoxProblem& p, unsigned* errors, hipStream_t 
 
 hipError_t launch_neox_plain(const NeoxProblem& p, unsigned* errors, hipStream_t stream, int cu_count) {
     NeoxArgs a = make_args(p, errors);
-    a.q_items = p.tokens * p.q_heads * (p.D / 2);
+    a.q_items = p.tokens * p.q_heads * (p.D / 2);  // each below 2^31: tensors have fewer than 2^32 elements
     a.k_items = p.tokens * p.k_heads * (p.D / 2);
-    const uint32_t total = a.q_items + a.k_items;
-    const uint32_t want = (total + 255) / 256;
+    const uint64_t total = uint64_t(a.q_items) + a.k_items;
+    const uint32_t want = static_cast<uint32_t>((total + 255) / 256);
     const uint32_t cap = static_cast<uint32_t>(cu_count > 0 ? cu_count : 256) * 32u;
     const uint32_t blocks = want < cap ? want : cap;
     if (blocks == 0) return hipSuccess;

@@ -459,6 +459,11 @@ def test_neox_precheck_rules():
     assert call_neox_can_use(*good[:9], pos + 4, *good[10:]) == (0, "ALIGN")
     assert call_neox_can_use(*good[:10], cache + 2, *good[11:]) == (0, "ALIGN")
     assert call_neox_can_use(*good[:5], 1 << 20, 1 << 10, 2, 64, *good[9:]) == (0, "TOO_LARGE")
+    # the size limit: fewer than 2^32 elements per tensor (2^25 tokens x 128 = 2^32 is refused)
+    far = [base + i * (1 << 40) for i in range(6)]
+    big = (far[0], far[1], far[2], far[3], bf, 1 << 25, 1, 1, 128, far[4], far[5], f32, 128)
+    assert call_neox_can_use(*big) == (0, "TOO_LARGE")
+    assert call_neox_can_use(*big[:8], 126, *big[9:])[1] in ("NOT_DEVICE_PTR", "OK")  # past the host rules
     assert call_neox_can_use(q + 64, *good[1:]) == (0, "OVERLAP")        # partial overlap of q_out and q
     assert call_neox_can_use(qo, cache + 16, *good[2:]) == (0, "OVERLAP")  # k_out over the cache
     assert call_neox_can_use(pos, *good[1:]) == (0, "OVERLAP")             # q_out over the positions

@@ -209,3 +209,31 @@ def test_more_tokens_than_the_fast_grid_holds_use_the_plain_kernel():
     for x, out in ((dq, qo), (dk, ko)):
         want = nx.neox_rope(to_host(x[idx], oracle.BF16), oracle.BF16, pos, cache, oracle.F32)
         assert_bitexact(to_host(out[idx], oracle.BF16), want, oracle.BF16, "sampled tokens")
+
+
+def test_tensors_of_more_than_2_to_the_31_elements():
+    """2^23 tokens of one query and one KV head of head_dim 384 in bf16: 3,221,225,472 elements per
+    tensor (between 2^31 and 2^32, 6.4 GB), drawn on the device.  The fast kernel against the plain
+    kernel over the whole output, and sampled tokens (the last included) against the oracle."""
+    tokens, D, maxp = 1 << 23, 384, 4096
+    log("2^23 tokens x 384: generating inputs on the device")
+    dq, dk, dpos = workloads.generate_neox_device(tokens, 1, 1, D, maxp, 77, DEV)
+    w = workloads.NeoxWorkload("big", oracle.BF16, 16, 1, 1, D, maxp, oracle.BF16, "random", 33)
+    _, _, _, cache = workloads.generate_neox(w)
+    dcache = to_dev(cache, oracle.BF16)
+    fq, fk = rla.neox_apply_qk(dq, dk, dpos, dcache)
+    rla.set_option(rla.OPT_PATH, 2)
+    pq, pk = rla.neox_apply_qk(dq, dk, dpos, dcache)
+    torch.cuda.synchronize()
+    s = rla.stats()
+    assert s["fast_launches"] == 1 and s["plain_launches"] == 1
+    assert torch.equal(fq.view(torch.int16), pq.view(torch.int16))
+    assert torch.equal(fk.view(torch.int16), pk.view(torch.int16))
+    del pq, pk
+    ids = workloads.sample_tokens(tokens, 1500, seed=8)
+    idx = torch.from_numpy(ids).to(DEV)
+    pos = dpos[idx].cpu().numpy()
+    for x, out in ((dq, fq), (dk, fk)):
+        want = nx.neox_rope(to_host(x[idx], oracle.BF16), oracle.BF16, pos, cache, oracle.BF16)
+        assert_bitexact(to_host(out[idx], oracle.BF16), want, oracle.BF16, "sampled tokens")
+    assert rla.neox_position_errors(0) == 0
