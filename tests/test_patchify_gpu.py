@@ -156,3 +156,29 @@ def test_4k_clip_of_more_than_2_to_the_31_elements():
         np.testing.assert_array_equal(got, want)
     st = rla.stats()
     assert st["fast_launches"] == 2 and st["plain_launches"] == 1
+
+
+@pytest.mark.parametrize("seed", [5, 6])
+def test_random_configurations(seed):
+    """Twenty seeded random configurations per seed: element sizes 1/2/4/8, p in {2, 3, 4, 8, 16},
+    widths that do or do not allow the LDS kernels, both directions, against the oracle."""
+    rng = np.random.default_rng(seed)
+    for i in range(20):
+        eb = int(rng.choice([1, 2, 4, 8]))
+        p = int(rng.choice([2, 3, 4, 8, 16]))
+        E = 16 // eb
+        unit = p * E if (rng.random() < 0.7 and p != 3) else p  # W a multiple of p*E: LDS kernels
+        W = unit * int(rng.integers(1, max(2, 512 // unit) + 1))
+        H = p * int(rng.integers(1, 5))
+        shape = (int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 4)), H, W)
+        x = workloads.generate_patch(shape, eb, seed=seed * 100 + i)
+        rla.stats_reset()
+        y = rla.patchify(to_dev(x), p)
+        back = rla.unpatchify(y, p)
+        torch.cuda.synchronize()
+        want = pf.patchify(x, p)
+        np.testing.assert_array_equal(to_host(y, want), want, err_msg=f"{shape} p={p} eb={eb}")
+        np.testing.assert_array_equal(to_host(back, x), x, err_msg=f"{shape} p={p} eb={eb} inverse")
+        fast = p in (2, 4, 8, 16) and W % (p * E) == 0
+        st = rla.stats()
+        assert (st["fast_launches"], st["plain_launches"]) == ((2, 0) if fast else (0, 2)), (shape, p, eb)
