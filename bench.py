@@ -117,6 +117,9 @@ def parse():
                     help="rope3d: run the workload's geometry in this dtype (auto: the workload's own)")
     ap.add_argument("--split", default="",
                     help="rope3d: dim_t,dim_h,dim_w instead of the workload's split (same head_dim)")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="rope3d: this many heads instead of the workload's (e.g. one GPU's share under "
+                         "head parallelism)")
     ap.add_argument("--graph", action="store_true",
                     help="rope3d: capture the K timed launches in one HIP graph and time its replay "
                          "(for the launch-bound small workloads); the default is eager launches")
@@ -173,6 +176,10 @@ def main():
         if len(split) != 3 or sum(split) != w.head_dim:
             raise SystemExit(f"--split needs three even widths summing to head_dim {w.head_dim}")
         w = dataclasses.replace(w, split=split, name=f"{w.name}_split{'_'.join(map(str, split))}")
+    if args.heads:
+        if args.heads < 1:
+            raise SystemExit("--heads must be positive")
+        w = dataclasses.replace(w, heads=args.heads, name=f"{w.name}_heads{args.heads}")
     gi = args.grid
     B, T, H, W, heads, D = w.shape(gi)
     numel = w.numel(gi)

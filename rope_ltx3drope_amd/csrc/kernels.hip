@@ -186,6 +186,7 @@ struct FastArgs {
     uint32_t HV;       // 16-B vectors per token (heads * V)
     uint32_t V;        // 16-B vectors per head
     uint32_t N, HW, W;
+    uint32_t T, H;     // grid sizes of the tensor (for the span decode's carries)
     uint32_t PT, PH;   // pairs in the t and h chunks
     uint32_t rowT4, rowH4, rowW4;  // float4 per table row of each section (kTabAligned)
     uint32_t offH4, offW4;         // first float4 of the h and w sections (kTabAligned)
@@ -217,21 +218,28 @@ struct FastArgs {
 // same vector of Q and of K; one-wavefront workgroups beat 128-1024 threads).
 // Both halves are one launch.
 //
-// WAVE_TOKEN: a token's heads*head_dim row is a whole number of wavefronts, so
-// each wavefront lies inside one token and the token -> (t, h, w) decode runs
-// once per wavefront on wave-uniform (scalar) values.  Otherwise each lane
-// decodes its own token.
+// DEC, how a lane finds its token -> (t, h, w):
+//  * kDecodeWave: a token's heads*head_dim row is a whole number of wavefronts,
+//    so each wavefront lies inside one token and the decode runs once per
+//    wavefront on wave-uniform (scalar) values;
+//  * kDecodeSpan: rows of 32 or more vectors that are not whole wavefronts; a
+//    wavefront then spans at most three tokens, its first token is decoded once
+//    and each lane steps 0, 1 or 2 tokens on from it (measured on one GPU's
+//    head share of the largest workload, 4 heads: about 2 % faster than a decode
+//    per lane);
+//  * kDecodeLane: every lane decodes its own token (rows below 32 vectors).
 //
 // Q and K are read with non-temporal hints and the results written with the
 // streaming store (sc1 | nt): every byte is touched exactly once, so the streams
 // should not displace other data from the caches (measured: +3 to +10 % on the
 // 0.8-6.8 GB workloads for the hints, about +1 % more for the store policy).
 enum : int { kTabAligned = 0, kTabPair = 1, kTabRow = 2 };
+enum : int { kDecodeLane = 0, kDecodeWave = 1, kDecodeSpan = 2 };
 constexpr uint32_t kTabRowMaxBytes = 4096;  // kTabRow's LDS row: head_dim <= 1024
 
-template <bool BF16, bool WAVE_TOKEN, int TAB>
+template <bool BF16, int DEC, int TAB>
 __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
-    static_assert(TAB != kTabRow || WAVE_TOKEN, "the LDS row needs one token per wavefront");
+    static_assert(TAB != kTabRow || DEC == kDecodeWave, "the LDS row needs one token per wavefront");
     constexpr uint32_t PPV = BF16 ? 4 : 2;
     const uint32_t half = gridDim.x >> 1;
     const bool second = blockIdx.x >= half;  // wave-uniform
@@ -240,23 +248,44 @@ __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
     u32x4* __restrict__ dst = second ? a.k_out : a.q_out;
     const uint32_t g = blk * kFastBlock + threadIdx.x;
     uint32_t tok, u;
-    if constexpr (WAVE_TOKEN) {
+    if constexpr (DEC == kDecodeWave) {
         const uint32_t g0 = blk * kFastBlock;
         if (g0 >= a.total) return;  // whole wavefronts: total is a multiple of 64 here
         tok = fast_div(g0, a.div_HV);
         u = (g0 - tok * a.HV) + threadIdx.x;
+    } else if constexpr (DEC == kDecodeSpan) {
+        if (g >= a.total) return;
+        tok = fast_div(blk * kFastBlock, a.div_HV);  // the wavefront's first token (wave-uniform)
+        u = (blk * kFastBlock - tok * a.HV) + threadIdx.x;
     } else {
         if (g >= a.total) return;
         tok = fast_div(g, a.div_HV);
         u = g - tok * a.HV;
     }
     const uint32_t n = fast_mod(tok, a.div_N);
-    const uint32_t tl = fast_div(n, a.div_HW);  // local coordinates, then global ones
+    uint32_t tl = fast_div(n, a.div_HW);  // local coordinates, then global ones
     const uint32_t rem = n - tl * a.HW;
-    const uint32_t hl = fast_div(rem, a.div_W);
+    uint32_t hl = fast_div(rem, a.div_W);
+    uint32_t wl = rem - hl * a.W;
+    if constexpr (DEC == kDecodeSpan) {
+        // step 0, 1 or 2 tokens on from the wavefront's first (a row holds 32 or more vectors)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (u >= a.HV) {
+                u -= a.HV;
+                if (++wl == a.W) {
+                    wl = 0;
+                    if (++hl == a.H) {
+                        hl = 0;
+                        if (++tl == a.T) tl = 0;  // the next batch element starts at the grid's origin
+                    }
+                }
+            }
+        }
+    }
     const uint32_t t = tl + a.t_off;
     const uint32_t h = hl + a.h_off;
-    const uint32_t w = rem - hl * a.W + a.w_off;
+    const uint32_t w = wl + a.w_off;
     const uint32_t j0 = fast_mod(u, a.div_V) * PPV;  // first pair of this vector inside its head
     const u32x4 x = __builtin_nontemporal_load(src + g);
     float c[PPV], s[PPV];
@@ -424,24 +453,22 @@ bool fast_supported(const Problem& p) {
     return (p.D * es) % 16 == 0;  // head rows are whole 16-byte vectors; any even split
 }
 
-template <int TAB>
-hipError_t launch_fast_tab(const FastArgs& a, bool bf16, bool wave_token, uint32_t blocks, size_t lds,
-                           hipStream_t stream) {
-    if constexpr (TAB == kTabRow) {
-        if (bf16)
-            hipLaunchKernelGGL((rope_fast<true, true, kTabRow>), dim3(blocks), dim3(kFastBlock), lds, stream, a);
-        else
-            hipLaunchKernelGGL((rope_fast<false, true, kTabRow>), dim3(blocks), dim3(kFastBlock), lds, stream, a);
-    } else if (bf16 && wave_token) {
-        hipLaunchKernelGGL((rope_fast<true, true, TAB>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    } else if (bf16) {
-        hipLaunchKernelGGL((rope_fast<true, false, TAB>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    } else if (wave_token) {
-        hipLaunchKernelGGL((rope_fast<false, true, TAB>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    } else {
-        hipLaunchKernelGGL((rope_fast<false, false, TAB>), dim3(blocks), dim3(kFastBlock), 0, stream, a);
-    }
+template <int DEC, int TAB>
+hipError_t launch_fast_dt(const FastArgs& a, bool bf16, uint32_t blocks, size_t lds, hipStream_t stream) {
+    if (bf16)
+        hipLaunchKernelGGL((rope_fast<true, DEC, TAB>), dim3(blocks), dim3(kFastBlock), lds, stream, a);
+    else
+        hipLaunchKernelGGL((rope_fast<false, DEC, TAB>), dim3(blocks), dim3(kFastBlock), lds, stream, a);
     return hipGetLastError();
+}
+
+template <int TAB>
+hipError_t launch_fast_tab(const FastArgs& a, bool bf16, int dec, uint32_t blocks, hipStream_t stream) {
+    switch (dec) {
+        case kDecodeWave: return launch_fast_dt<kDecodeWave, TAB>(a, bf16, blocks, 0, stream);
+        case kDecodeSpan: return launch_fast_dt<kDecodeSpan, TAB>(a, bf16, blocks, 0, stream);
+        default: return launch_fast_dt<kDecodeLane, TAB>(a, bf16, blocks, 0, stream);
+    }
 }
 
 hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
@@ -459,6 +486,8 @@ hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
     a.N = p.T * p.H * p.W;
     a.HW = p.H * p.W;
     a.W = p.W;
+    a.T = p.T;
+    a.H = p.H;
     a.PT = p.PT;
     a.PH = p.PH;
     a.rowT4 = p.PT / 2;
@@ -487,9 +516,10 @@ hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
     const size_t row_bytes = size_t(p.D / 2) * 8;  // kTabRow's LDS: (cos, sin) of every pair of a head
     (void)device;
     if (wave_token && row_bytes <= kTabRowMaxBytes)
-        return launch_fast_tab<kTabRow>(a, bf16, true, blocks, row_bytes, stream);
-    if (aligned) return launch_fast_tab<kTabAligned>(a, bf16, wave_token, blocks, 0, stream);
-    return launch_fast_tab<kTabPair>(a, bf16, wave_token, blocks, 0, stream);
+        return launch_fast_dt<kDecodeWave, kTabRow>(a, bf16, blocks, row_bytes, stream);
+    const int dec = wave_token ? kDecodeWave : a.HV >= 32 ? kDecodeSpan : kDecodeLane;
+    if (aligned) return launch_fast_tab<kTabAligned>(a, bf16, dec, blocks, stream);
+    return launch_fast_tab<kTabPair>(a, bf16, dec, blocks, stream);
 }
 
 hipError_t launch_plain(const Problem& p, hipStream_t stream, int device) {
