@@ -39,6 +39,13 @@ def test_defaults_per_op():
     assert (a.steps, a.warmup) == (7, 3)
 
 
+def test_head_share_and_cpu_thread_options():
+    a = parse("--heads", "3")
+    assert a.heads == 3
+    assert 1 <= parse().cpu_threads <= 16
+    assert parse("--cpu-threads", "0").cpu_threads == 0
+
+
 def test_bad_step_counts_are_refused():
     for argv in (("--steps", "0"), ("--warmup", "-1"), ("--rotate", "-2")):
         with pytest.raises(SystemExit) as e:
