@@ -92,3 +92,29 @@ def test_planted_mistake_is_caught(monkeypatch, impl):
         except AssertionError:
             caught.append(name)
     assert caught
+
+
+def _unpatchify_h_w_swapped(y, p):
+    B, Cpp, F, Hp, Wp = y.shape
+    C = Cpp // (p * p)
+    x = y.reshape(B, C, p, p, F, Hp, Wp).transpose(0, 1, 4, 5, 2, 6, 3)  # reads (c, h-offset, w-offset)
+    return np.ascontiguousarray(x).reshape(B, C, F, Hp * p, Wp * p)
+
+
+def _unpatchify_frames_transposed(y, p):
+    B, Cpp, F, Hp, Wp = y.shape
+    C = Cpp // (p * p)
+    x = y.reshape(B, C, p, p, F, Hp, Wp).transpose(0, 4, 1, 5, 3, 6, 2)  # frames and channels swapped
+    return np.ascontiguousarray(x).reshape(B, C, F, Hp * p, Wp * p)
+
+
+@pytest.mark.parametrize("impl", [_unpatchify_h_w_swapped, _unpatchify_frames_transposed])
+def test_planted_mistake_in_the_inverse_is_caught(monkeypatch, impl):
+    monkeypatch.setattr(pf, "unpatchify", impl)
+    caught = []
+    for name, pin in ALL_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught.append(name)
+    assert caught
