@@ -193,6 +193,14 @@ def test_refcount_frees_when_last_reference_goes():
     t.close()
     assert rla.stats()["tables_alive"] == alive0
     assert L.ltx3drope_tables_release(None) == _lib.E_INVALID
+    # a closed handle refuses further use instead of touching freed memory; closing twice is harmless
+    with pytest.raises(ValueError):
+        t.describe()
+    t.close()
+    with rla.tables_build(3, 3, 3, (2, 2, 2)) as t2:
+        assert t2.grid == (3, 3, 3) and t2.split == (2, 2, 2)
+    with pytest.raises(ValueError):
+        t2.read()
 
 
 def test_concurrent_builds_are_consistent():
