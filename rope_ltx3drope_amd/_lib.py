@@ -87,6 +87,13 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"ltx3drope HIP library not found at {LIB_PATH}; build it with "
                 "`python -m rope_ltx3drope_amd.build` (there is no CPU fallback)")
+        # torch first: its HIP runtime must be the process's one.  torch links the runtime under
+        # another name than this library does, so loading this library first would bring in a
+        # second runtime, to which torch's streams and allocations are unknown.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         sig = {
             "ltx3drope_tables_build": (ctypes.c_int, [ctypes.c_int, i64, i64, i64, i64, i64, i64, ctypes.c_double, vp,
