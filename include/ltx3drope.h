@@ -257,7 +257,9 @@ int ltx3drope_apply_qk_shard(void* q_out, void* k_out, const void* q, const void
  * (odd head_dim), ALIGN (element alignment; positions 8 B), OVERLAP,
  * TOO_LARGE (a tensor or the cache of 2^32 elements or more, or a size of
  * 2^31 or more), NOT_DEVICE_PTR,
- * TABLE_DEVICE (pointers on different devices), EXTENT.  apply_qk returns
+ * TABLE_DEVICE (pointers on different devices), EXTENT.  can_use accepts
+ * q_out and k_out both NULL (fresh outputs: only the inputs are checked);
+ * apply_qk needs both.  apply_qk returns
  * E_UNSUPPORTED for any of these; the first call on a device allocates the
  * device's 256-byte counter (E_NOMEM when out of memory, E_HIP for another
  * HIP failure), and a failed launch gives E_HIP.
@@ -327,13 +329,14 @@ int ltx3drope_stats(ltx3drope_stats_t* out);
 int ltx3drope_stats_reset(void);
 
 /* Which kernel apply_qk would use for these arguments when the gate trusts the fast path:
-   1 fast, 2 plain, or a negative status if the precheck fails. */
+   1 fast, 2 plain, or a negative status if the precheck fails (host rules only: device memory is
+   not queried).  q_out and k_out may both be NULL: fresh outputs, which are 16-byte aligned. */
 int ltx3drope_kernel_choice(const void* q_out, const void* k_out, const void* q, const void* k,
                             int dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads,
                             int64_t head_dim, ltx3drope_tables_t tables);
 
 /* Measurement helper: copy `bytes` (a multiple of 16, fewer than 2^32 - 64 vectors of 16 B, both
-   pointers 16-B aligned, non-overlapping device memory) from src to dst with a plain streaming kernel
+   pointers 16-B aligned, non-overlapping memory of one device) from src to dst with a plain streaming kernel
    on `stream` (the fast kernel's launch shape and cache hints, one read and one write stream); used
    as the bandwidth ceiling and to calibrate traffic counters.  E_INVALID on bad arguments, E_HIP. */
 int ltx3drope_copy(void* dst, const void* src, int64_t bytes, void* stream);

@@ -296,11 +296,10 @@ def neox_can_use(q, k, positions, cache, q_out=None, k_out=None) -> Tuple[bool, 
         _neox_marshal(q, k, positions, cache, q_out, k_out)
     except Ltx3dRopeUnsupported as e:
         return False, e.reason
-    torch = _torch()
-    qo = q_out if q_out is not None else torch.empty_like(q)
-    ko = k_out if k_out is not None else torch.empty_like(k)
+    if (q_out is None) != (k_out is None):
+        raise ValueError("give both q_out and k_out, or neither")
     reason = ctypes.c_int(0)
-    ok = _lib.lib().ltx3drope_neox_can_use(*_neox_args(qo, ko, q, k, positions, cache), ctypes.byref(reason))
+    ok = _lib.lib().ltx3drope_neox_can_use(*_neox_args(q_out, k_out, q, k, positions, cache), ctypes.byref(reason))
     return bool(ok), _lib.REASONS.get(reason.value, str(reason.value))
 
 
@@ -402,12 +401,13 @@ def dit_freq_grid(theta: float, dim: int, num_rope_elems: int, double_precision:
 
 def kernel_choice(q, k, tabs: Tables, q_out=None, k_out=None) -> str:
     """'fast' or 'plain': the kernel apply_qk uses once the gate trusts the fast path."""
-    torch = _torch()
     B, T, H, W, heads, D = _shape6(q)
-    qo = q_out if q_out is not None else torch.empty_like(q)
-    ko = k_out if k_out is not None else torch.empty_like(k)
-    r = _lib.lib().ltx3drope_kernel_choice(qo.data_ptr(), ko.data_ptr(), q.data_ptr(), k.data_ptr(), _dtype_code(q),
-                                           B, T, H, W, heads, D, tabs.handle)
+    if (q_out is None) != (k_out is None):
+        raise ValueError("give both q_out and k_out, or neither")
+    qo = q_out.data_ptr() if q_out is not None else None
+    ko = k_out.data_ptr() if k_out is not None else None
+    r = _lib.lib().ltx3drope_kernel_choice(qo, ko, q.data_ptr(), k.data_ptr(), _dtype_code(q), B, T, H, W, heads, D,
+                                           tabs.handle)
     if r < 0:
         raise Ltx3dRopeError(r, "kernel_choice")
     return {1: "fast", 2: "plain"}[r]

@@ -387,10 +387,11 @@ int apply_impl(void* q_out, void* k_out, const void* q, const void* k, int dtype
 
 // ---- rotate-half RoPE with a gathered cache -------------------------------
 
+// With check_outputs false, q_out and k_out are ignored (fresh outputs, which cannot overlap anything).
 int neox_precheck(const void* q_out, const void* k_out, const void* q, const void* k, int dtype, int64_t tokens,
                   int64_t q_heads, int64_t k_heads, int64_t D, const int64_t* positions, const void* cache,
-                  int cache_dtype, int64_t max_position, bool check_memory, int* device_out) {
-    if (!q_out || !k_out || !q || !k || !positions || !cache) return LTX3DROPE_REASON_NULLPTR;
+                  int cache_dtype, int64_t max_position, bool check_memory, bool check_outputs, int* device_out) {
+    if ((check_outputs && (!q_out || !k_out)) || !q || !k || !positions || !cache) return LTX3DROPE_REASON_NULLPTR;
     for (int d : {dtype, cache_dtype})
         if (d != LTX3DROPE_DTYPE_F32 && d != LTX3DROPE_DTYPE_BF16) return LTX3DROPE_REASON_DTYPE;
     if (tokens <= 0 || q_heads <= 0 || k_heads <= 0 || D <= 0 || max_position <= 0)
@@ -399,7 +400,7 @@ int neox_precheck(const void* q_out, const void* k_out, const void* q, const voi
     const size_t es = dtype == LTX3DROPE_DTYPE_F32 ? 4 : 2;
     const size_t cs = cache_dtype == LTX3DROPE_DTYPE_F32 ? 4 : 2;
     for (const void* p : {q_out, k_out, q, k})
-        if (reinterpret_cast<uintptr_t>(p) % es) return LTX3DROPE_REASON_ALIGN;
+        if (reinterpret_cast<uintptr_t>(p) % es) return LTX3DROPE_REASON_ALIGN;  // NULL outputs pass
     if (reinterpret_cast<uintptr_t>(cache) % cs || reinterpret_cast<uintptr_t>(positions) % 8)
         return LTX3DROPE_REASON_ALIGN;
     // fewer than 2^32 elements per tensor (and per cache), each size below 2^31
@@ -419,13 +420,16 @@ int neox_precheck(const void* q_out, const void* k_out, const void* q, const voi
     const size_t pb = static_cast<size_t>(tokens) * 8;
     const size_t cb = static_cast<size_t>(max_position * D) * cs;
     // outputs: exact aliasing with their own input is allowed; nothing else may overlap an output
-    if ((q_out != q && ranges_overlap(q_out, qb, q, qb)) || ranges_overlap(q_out, qb, k, kb) ||
-        ranges_overlap(k_out, kb, q, qb) || (k_out != k && ranges_overlap(k_out, kb, k, kb)) ||
-        ranges_overlap(q_out, qb, k_out, kb))
-        return LTX3DROPE_REASON_OVERLAP;
-    for (const void* o : {q_out, k_out}) {
-        const size_t ob = o == q_out ? qb : kb;
-        if (ranges_overlap(o, ob, positions, pb) || ranges_overlap(o, ob, cache, cb)) return LTX3DROPE_REASON_OVERLAP;
+    if (check_outputs) {
+        if ((q_out != q && ranges_overlap(q_out, qb, q, qb)) || ranges_overlap(q_out, qb, k, kb) ||
+            ranges_overlap(k_out, kb, q, qb) || (k_out != k && ranges_overlap(k_out, kb, k, kb)) ||
+            ranges_overlap(q_out, qb, k_out, kb))
+            return LTX3DROPE_REASON_OVERLAP;
+        for (const void* o : {q_out, k_out}) {
+            const size_t ob = o == q_out ? qb : kb;
+            if (ranges_overlap(o, ob, positions, pb) || ranges_overlap(o, ob, cache, cb))
+                return LTX3DROPE_REASON_OVERLAP;
+        }
     }
     if (check_memory) {
         hipPointerAttribute_t a;
@@ -438,8 +442,9 @@ int neox_precheck(const void* q_out, const void* k_out, const void* q, const voi
         const int device = a.device;
         const std::pair<const void*, size_t> spans[6] = {{q, qb}, {k, kb}, {q_out, qb}, {k_out, kb},
                                                          {positions, pb}, {cache, cb}};
-        for (const auto& sp : spans) {
-            const int r = check_device_ptr(sp.first, sp.second, device);
+        for (int i = 0; i < 6; ++i) {
+            if (!check_outputs && (i == 2 || i == 3)) continue;  // the outputs
+            const int r = check_device_ptr(spans[i].first, spans[i].second, device);
             if (r != LTX3DROPE_REASON_OK) return r;
         }
         if (device_out) *device_out = device;
@@ -534,7 +539,8 @@ int ltx3drope_can_use_shard(const void* q_out, const void* k_out, const void* q,
 int ltx3drope_kernel_choice(const void* q_out, const void* k_out, const void* q, const void* k, int dtype, int64_t B,
                             int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
                             ltx3drope_tables_t tables) {
-    const int r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, false, true, Placement());
+    const bool outputs = q_out != nullptr || k_out != nullptr;
+    const int r = precheck(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, false, outputs, Placement());
     if (r != LTX3DROPE_REASON_OK) return status_for_reason(r);
     const Problem p = make_problem(const_cast<void*>(q_out), const_cast<void*>(k_out), q, k, dtype, B, T, H, W, heads,
                                    head_dim, tables, Placement());
@@ -562,8 +568,9 @@ int ltx3drope_neox_can_use(const void* q_out, const void* k_out, const void* q, 
                            int64_t tokens, int64_t q_heads, int64_t k_heads, int64_t head_dim,
                            const int64_t* positions, const void* cache, int cache_dtype, int64_t max_position,
                            int* reason) {
+    const bool outputs = q_out != nullptr || k_out != nullptr;
     const int r = neox_precheck(q_out, k_out, q, k, dtype, tokens, q_heads, k_heads, head_dim, positions, cache,
-                                cache_dtype, max_position, true, nullptr);
+                                cache_dtype, max_position, true, outputs, nullptr);
     if (reason) *reason = r;
     return r == LTX3DROPE_REASON_OK ? 1 : 0;
 }
@@ -573,7 +580,7 @@ int ltx3drope_neox_apply_qk(void* q_out, void* k_out, const void* q, const void*
                             const void* cache, int cache_dtype, int64_t max_position, void* stream_ptr) {
     int device = -1;
     const int r = neox_precheck(q_out, k_out, q, k, dtype, tokens, q_heads, k_heads, head_dim, positions, cache,
-                                cache_dtype, max_position, true, &device);
+                                cache_dtype, max_position, true, true, &device);
     if (r != LTX3DROPE_REASON_OK) {
         stats().rejected.fetch_add(1);
         return LTX3DROPE_E_UNSUPPORTED;
@@ -768,7 +775,7 @@ int ltx3drope_copy(void* dst, const void* src, int64_t bytes, void* stream) {
         return LTX3DROPE_E_INVALID;
     if (ranges_overlap(dst, static_cast<size_t>(bytes), src, static_cast<size_t>(bytes))) return LTX3DROPE_E_INVALID;
     if (bytes / 16 >= (int64_t(1) << 32) - 64) return LTX3DROPE_E_INVALID;
-    int device = 0;
+    int device = -1;
     for (const void* p : {static_cast<const void*>(dst), src}) {
         hipPointerAttribute_t a;
         std::memset(&a, 0, sizeof(a));
@@ -776,6 +783,7 @@ int ltx3drope_copy(void* dst, const void* src, int64_t bytes, void* stream) {
             (void)hipGetLastError();
             return LTX3DROPE_E_INVALID;
         }
+        if (device >= 0 && a.device != device) return LTX3DROPE_E_INVALID;  // both on one device
         device = a.device;
         void* base = nullptr;
         size_t size = 0;

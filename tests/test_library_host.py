@@ -358,6 +358,12 @@ def test_kernel_choice_rules():
     with rla.tables_build(2, 3, 4, (4, 8, 4)) as tab:  # chunk widths not multiples of a vector's pairs
         assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_F32, 1, 2, 3, 4, 2, 16, tab.handle) == 1
         assert L.ltx3drope_kernel_choice(qo, ko, q, k, _lib.DTYPE_BF16, 1, 2, 3, 4, 2, 16, tab.handle) == 1
+    # NULL outputs stand for fresh (aligned) outputs: only the inputs decide; one NULL is refused
+    with rla.tables_build(2, 3, 4, (32, 48, 48)) as tab:
+        shp = (1, 2, 3, 4, 16, 128)
+        assert L.ltx3drope_kernel_choice(None, None, q, k, _lib.DTYPE_BF16, *shp, tab.handle) == 1
+        assert L.ltx3drope_kernel_choice(None, None, q + 4, k, _lib.DTYPE_BF16, *shp, tab.handle) == 2
+        assert L.ltx3drope_kernel_choice(qo, None, q, k, _lib.DTYPE_BF16, *shp, tab.handle) == _lib.E_UNSUPPORTED
 
 
 # ---------------------------------------------------------------------------
@@ -479,6 +485,11 @@ def test_neox_precheck_rules():
     # exact in-place aliasing passes every host rule (device memory is checked last)
     ok, reason = call_neox_can_use(q, k, *good[2:])
     assert reason in ("NOT_DEVICE_PTR", "OK")
+    # both outputs NULL: fresh outputs, only the inputs are checked; one NULL output is refused
+    assert call_neox_can_use(None, None, *good[2:])[1] in ("NOT_DEVICE_PTR", "OK")
+    assert call_neox_can_use(None, None, q + 1, *good[3:]) == (0, "ALIGN")
+    assert call_neox_can_use(None, None, *good[2:5], 1 << 20, 1 << 10, 2, 64, *good[9:]) == (0, "TOO_LARGE")
+    assert call_neox_can_use(qo, None, *good[2:]) == (0, "NULLPTR")
 
 
 # ---------------------------------------------------------------------------

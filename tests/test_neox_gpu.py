@@ -156,7 +156,14 @@ def test_precheck_refusals_on_device():
     q, k, pos, cache = workloads.generate_neox(w)
     dq, dk = to_dev(q, w.dtype), to_dev(k, w.dtype)
     dpos, dcache = torch.from_numpy(pos).to(DEV), to_dev(cache, w.cache_dtype)
+    before = torch.cuda.memory_allocated(DEV)
     assert rla.neox_can_use(dq, dk, dpos, dcache) == (True, "OK")
+    assert torch.cuda.memory_allocated(DEV) == before  # the query allocates nothing
+    qo, ko = torch.empty_like(dq), torch.empty_like(dk)
+    assert rla.neox_can_use(dq, dk, dpos, dcache, qo, ko) == (True, "OK")
+    assert rla.neox_can_use(dq, dk, dpos, dcache, dq, dk) == (True, "OK")  # exact in-place aliasing
+    with pytest.raises(ValueError):
+        rla.neox_can_use(dq, dk, dpos, dcache, qo, None)
     assert rla.neox_can_use(dq, dk, dpos.int(), dcache)[0] is False
     assert rla.neox_can_use(dq, dk, dpos.cpu(), dcache) == (False, "NOT_DEVICE_PTR")
     with pytest.raises(rla.Ltx3dRopeUnsupported):
