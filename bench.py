@@ -237,9 +237,10 @@ def main():
             rla.apply_qk(q, k, tab, torch.empty_like(q), torch.empty_like(k))
         torch.cuda.synchronize()
 
-    # the warmup keeps outputs alive as the timed loop does (the last `rotate` sets), so the
-    # allocator already holds every block the timed steps need: no device allocation inside
-    # the timed region
+    # the output blocks of rotate + 1 steps are reserved once, and the warmup keeps outputs alive
+    # as the timed loop does (the last `rotate` sets): no device allocation inside the timed region
+    if not (args.inplace or args.reuse_outputs or args.graph):
+        reserve_outputs((q.shape, k.shape), q.dtype, dev, rotate + 1)
     outs = []
     for _ in range(args.warmup):
         outs.append(step())
@@ -262,11 +263,13 @@ def main():
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        seg0 = device_segments(dev)
         t0 = time.perf_counter()
         e0.record(stream)
         g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
+        new_segments = device_segments(dev) - seg0
         wall = time.perf_counter() - t0
         tab.close()
         qo, ko = outs_static[(args.steps - 1) % rotate]
@@ -277,6 +280,7 @@ def main():
         # ~20 us per step, the kernel ~1 ms), and no marker sits between two kernels
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        seg0 = device_segments(dev)
         t0 = time.perf_counter()
         e0.record(stream)
         for _ in range(args.steps):
@@ -285,6 +289,7 @@ def main():
                 outs.pop(0)  # keep `rotate` output sets alive so the allocator cannot hand back a cached one
         e1.record(stream)
         torch.cuda.synchronize()
+        new_segments = device_segments(dev) - seg0
         qo, ko = outs[-1]
         last_in = (args.steps + args.warmup - 1) % rotate
         wall = time.perf_counter() - t0
@@ -347,6 +352,7 @@ def main():
         "gelem_per_s": round(elems / (wall / args.steps) / 1e9, 2),
         "kernel": kernel,
         "kernel_avg_us": round(kavg_s * 1e6, 2),
+        "timed_region_device_allocations": new_segments,
         "copy_ceiling_GBps": None if copy_gbs is None else round(copy_gbs, 1),
         "parity": {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -385,6 +391,8 @@ def main_neox(args):
     sets = [(q, k)] + [(q.clone(), k.clone()) for _ in range(rotate - 1)]
     stream = torch.cuda.current_stream(dev)
     reused = [(torch.empty_like(a), torch.empty_like(b)) for a, b in sets] if args.reuse_outputs else []
+    if not args.reuse_outputs:
+        reserve_outputs((q.shape, k.shape), q.dtype, dev, rotate + 1)
     outs = []
 
     def step(i):
@@ -402,12 +410,14 @@ def main_neox(args):
         step(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    seg0 = device_segments(dev)
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(args.steps):
         step(args.warmup + i)
     e1.record(stream)
     torch.cuda.synchronize()
+    new_segments = device_segments(dev) - seg0
     wall = time.perf_counter() - t0
     kavg = e0.elapsed_time(e1) / args.steps / 1e3  # launches run back to back: no marker between them
     qo, ko = outs[-1]
@@ -435,6 +445,7 @@ def main_neox(args):
                    "outputs": "reused" if args.reuse_outputs else "fresh"},
         "kernel": kernel,
         "kernel_avg_us": round(kavg * 1e6, 2),
+        "timed_region_device_allocations": new_segments,
         "copy_ceiling_GBps": round(copy_gbs, 1),
         "parity": {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0},
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -529,6 +540,10 @@ def main_patch(args):
         del out_like
         fn_out = (lambda t, o: rla.unpatchify(t, p, out=o)) if inverse else (lambda t, o: rla.patchify(t, p, out=o))
     stream = torch.cuda.current_stream(dev)
+    if not args.reuse_outputs:
+        B_, C_, F_, H_, W_ = x.shape
+        out_shape = x.shape if inverse else (B_, C_ * p * p, F_, H_ // p, W_ // p)
+        reserve_outputs((out_shape,), x.dtype, dev, rotate + 1)
     outs = []
 
     def step(i):
@@ -543,12 +558,14 @@ def main_patch(args):
         step(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    seg0 = device_segments(dev)
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(args.steps):
         step(args.warmup + i)
     e1.record(stream)
     torch.cuda.synchronize()
+    new_segments = device_segments(dev) - seg0
     wall = time.perf_counter() - t0
     kavg = e0.elapsed_time(e1) / args.steps / 1e3  # launches run back to back: no marker between them
     got = outs[-1].cpu().numpy().view(x_np.dtype)
@@ -596,6 +613,7 @@ def main_patch(args):
                    "outputs": "reused" if args.reuse_outputs else "fresh"},
         "kernel": kernel,
         "kernel_avg_us": round(kavg * 1e6, 2),
+        "timed_region_device_allocations": new_segments,
         "copy_ceiling_GBps": round(copy_gbs, 1),
         "parity": {"compared_elements": int(got.size), "mismatching_elements": mism, "tolerance_ulp": 0},
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -605,6 +623,23 @@ def main_patch(args):
     print(json.dumps(line), flush=True)
     if mism:
         sys.exit(1)
+
+
+def device_segments(dev) -> int:
+    """Device memory segments torch's caching allocator has obtained so far (each one a hipMalloc)."""
+    import torch
+
+    return int(torch.cuda.memory_stats(dev).get("segment.all.allocated", 0))
+
+
+def reserve_outputs(shapes, dtype, dev, count: int) -> None:
+    """Makes torch's caching allocator hold `count` sets of output blocks of these shapes: the
+    timed loop keeps `rotate` sets alive and allocates one more per step, so with rotate + 1 sets
+    cached no step inside the timed region needs a new device allocation."""
+    import torch
+
+    held = [[torch.empty(sh, dtype=dtype, device=dev) for sh in shapes] for _ in range(count)]
+    del held
 
 
 def copy_ceiling(sets, stream, reps_per_set: int = 10) -> float:

@@ -44,6 +44,8 @@ def test_bench_line(capsys, monkeypatch, argv):
     assert d["n_gpus"] == 1 and d["value"] > 0 and d["steps"] == int(argv[argv.index("--steps") + 1])
     assert d["parity"]["mismatching_elements"] == 0
     assert "workload" in d["config"]
+    if "timed_region_device_allocations" in d:  # outputs are reserved before the warmup
+        assert d["timed_region_device_allocations"] == 0
     if d["roofline"] is not None:
         r = d["roofline"]
         assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
