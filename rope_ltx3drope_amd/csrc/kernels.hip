@@ -23,10 +23,12 @@
 //    (8 bf16 or 4 fp32 values, i.e. 4 or 2 pairs): the first half of the grid
 //    covers Q, the second half K.  When a token's heads*head_dim row is a whole
 //    number of wavefronts, the token -> (t, h, w) decode runs once per
-//    wavefront on scalar values and the wavefront assembles the token's
-//    (cos, sin) row in LDS; otherwise each lane reads its vector's row segment
-//    from the packed tables, which stay in the L1/L2 caches (they are tens of
-//    KB).  Q and K stream through with non-temporal 16-byte loads and
+//    wavefront on scalar values and (head_dim <= 1024) the wavefront assembles
+//    the token's (cos, sin) row in LDS.  Otherwise the decode runs once per
+//    wavefront plus a step of 0-2 tokens per lane (rows of 32+ vectors) or per
+//    lane, and each lane reads its vector's row segment from the packed
+//    tables, which stay in the L1/L2 caches (they are tens of KB).  Q and K
+//    stream through with non-temporal 16-byte loads and
 //    streaming (sc1 | nt) 16-byte stores; bf16 results are packed with the
 //    hardware's round-to-nearest-even conversion (v_cvt_pk_bf16_f32).
 //    Measured on MI355X, this shape streams faster than a persistent grid with
