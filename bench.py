@@ -127,6 +127,9 @@ def parse():
                     help="rope3d: write into output buffers allocated once per input set instead of fresh ones")
     ap.add_argument("--inplace", action="store_true",
                     help="rope3d: rotate Q and K in place instead of into fresh outputs")
+    ap.add_argument("--cycle", action="store_true",
+                    help="rope3d: one step = the workload's whole call sequence over its grids (workload 5: "
+                         "(G1, G2, G3) x 4 from the table cache; workload 3: its 24 calls), fresh outputs")
     ap.add_argument("--rotate", type=int, default=0,
                     help="cycle through this many input/output sets (0: enough to exceed 2x the 256 MB "
                          "Infinity Cache, so every step streams from HBM)")
@@ -158,6 +161,10 @@ def main():
         return main_patch(args)
     if args.op == "dit_freqs":
         return main_dit(args)
+    if args.cycle:
+        if args.graph or args.inplace or args.reuse_outputs or args.heads or args.split or args.dtype != "auto":
+            raise SystemExit("--cycle times the workload as defined: no other rope3d option applies")
+        return main_cycle(args)
 
     import numpy as np
     import torch
@@ -359,6 +366,126 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    if mism:
+        sys.exit(1)
+
+
+def main_cycle(args):
+    """The fused 3D RoPE over a workload's whole call sequence: one step = every call of the
+    sequence, each on its own grid's inputs with fresh outputs, its tables from the cache (one
+    build per grid, in the warmup)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import rope_ltx3drope_amd as rla
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    grids = sorted(set(w.calls))
+    t0 = time.perf_counter()
+    host = workloads.generate(w, grids)
+    print(f"[bench] inputs of {len(grids)} grid(s) generated in {time.perf_counter() - t0:.1f} s: {w.name}",
+          file=sys.stderr, flush=True)
+    tdt = torch.bfloat16 if w.itemsize == 2 else torch.float32
+
+    def to_dev(x):
+        return (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if w.itemsize == 2
+                else torch.from_numpy(x)).to(dev)
+
+    inputs = {gi: (to_dev(q), to_dev(k)) for gi, (q, k) in zip(grids, host)}
+    alg_pass = sum(w.algorithmic_bytes(gi) for gi in w.calls)
+    elems_pass = sum(2 * w.numel(gi) for gi in w.calls)
+    stream = torch.cuda.current_stream(dev)
+    last = {}  # grid -> its latest outputs (the previous ones are released after the next call's allocation)
+
+    def call(gi):
+        q, k = inputs[gi]
+        T, H, W = w.grids[gi]
+        tab = rla.tables_build(T, H, W, w.split, w.base, device=0)
+        qo, ko = torch.empty_like(q), torch.empty_like(k)
+        rla.apply_qk(q, k, tab, qo, ko)
+        tab.close()
+        last[gi] = (qo, ko)
+
+    def step():
+        for gi in w.calls:
+            call(gi)
+
+    # two output sets per grid reserved up front: no device allocation inside the timed region
+    for gi in grids:
+        reserve_outputs((inputs[gi][0].shape, inputs[gi][1].shape), tdt, dev, 2)
+    rla.cache_clear()
+    rla.stats_reset()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    warm = rla.stats()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    seg0 = device_segments(dev)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    new_segments = device_segments(dev) - seg0
+    st = rla.stats()
+    kernel = "rope_fast" if st["fast_launches"] > 0 and st["gate_disabled"] == 0 else "rope_plain"
+    calls = args.steps * len(w.calls)
+    gpu_s = e0.elapsed_time(e1) / 1e3
+    achieved = alg_pass * args.steps / gpu_s / 1e9
+    value = alg_pass / (wall / args.steps) / 1e9
+
+    # parity: sampled tokens of every grid's last outputs against the oracle
+    mism, sampled = 0, 0
+    for gi, (q_np, k_np) in zip(grids, host):
+        B, T, H, W, heads, D = w.shape(gi)
+        ids = workloads.sample_tokens(B * T * H * W, 128, seed=4321 + gi)
+        idx = torch.from_numpy(ids).to(dev)
+        for x_np, out in ((q_np, last[gi][0]), (k_np, last[gi][1])):
+            want = oracle.rope3d_sampled(x_np, w.dtype, w.split, ids, w.base)
+            got = out.view(B * T * H * W, heads, D)[idx].cpu()
+            got = got.view(torch.int16).numpy().view(np.uint16) if w.itemsize == 2 else got.numpy()
+            mism += int((got.view(want.dtype) != want).sum())
+        sampled += len(ids)
+    copy_gbs = copy_ceiling([inputs[grids[0]]], stream)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), inputs resident in HBM)",
+        "config": {"workload": w.name + "_call_sequence", "B": w.B, "grids_THW": [list(g) for g in w.grids],
+                   "call_sequence": list(w.calls), "heads": w.heads, "head_dim": w.head_dim,
+                   "rope_dim_split": list(w.split), "base": w.base,
+                   "algorithmic_bytes_per_step": alg_pass, "parallelism": "single GPU", "launch": "eager",
+                   "outputs": "fresh"},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "gelem_per_s": round(elems_pass / (wall / args.steps) / 1e9, 2),
+        "kernel": kernel,
+        "kernel_avg_us": round(gpu_s / calls * 1e6, 2),
+        "timed_region_device_allocations": new_segments,
+        "table_cache": {"warmup_misses": warm["cache_misses"], "warmup_hits": warm["cache_hits"],
+                        "timed_misses": st["cache_misses"] - warm["cache_misses"],
+                        "timed_hits": st["cache_hits"] - warm["cache_hits"]},
+        "copy_ceiling_GBps": round(copy_gbs, 1),
+        "parity": {"sampled_tokens": sampled, "mismatching_elements": mism, "tolerance_ulp": 0},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
     if mism:

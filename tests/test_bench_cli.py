@@ -90,3 +90,11 @@ def test_traffic_record_is_used_only_for_the_source_it_was_taken_on(kernel):
         assert bench.measured_traffic(rec["workload"], kernel) == rec["bytes_per_launch"]
     else:
         assert bench.measured_traffic(rec["workload"], kernel) is None
+
+
+@pytest.mark.parametrize("extra", [("--graph",), ("--inplace",), ("--heads", "4"), ("--dtype", "f32")])
+def test_cycle_mode_refuses_other_rope_options(monkeypatch, extra):
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--cycle", *extra])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert "--cycle" in str(e.value.code)

@@ -36,7 +36,8 @@ def run_bench(capsys, monkeypatch, *argv):
     ("--op", "patchify", "--patch-workload", "p2", "--steps", "3", "--warmup", "2", "--no-cpu-baseline"),
     ("--op", "unpatchify", "--patch-workload", "p2", "--steps", "3", "--warmup", "2", "--no-cpu-baseline"),
     ("--op", "dit_freqs", "--steps", "3", "--warmup", "2"),
-], ids=["rope3d", "rope3d-graph", "rope3d-inplace", "neox", "patchify", "unpatchify", "dit"])
+    ("--workload", "3", "--cycle", "--steps", "2", "--warmup", "1"),
+], ids=["rope3d", "rope3d-graph", "rope3d-inplace", "neox", "patchify", "unpatchify", "dit", "rope3d-cycle"])
 def test_bench_line(capsys, monkeypatch, argv):
     rla.set_option(rla.OPT_PATH, 0)
     d = run_bench(capsys, monkeypatch, *argv)
@@ -50,3 +51,12 @@ def test_bench_line(capsys, monkeypatch, argv):
         r = d["roofline"]
         assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
         assert 0 < r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-3)
+
+
+def test_cycle_mode_reports_the_table_cache(capsys, monkeypatch):
+    """Workload 3's 24 calls as one step: one table build in the warmup, hits ever after."""
+    rla.set_option(rla.OPT_PATH, 0)
+    d = run_bench(capsys, monkeypatch, "--workload", "3", "--cycle", "--steps", "2", "--warmup", "1")
+    assert d["config"]["call_sequence"] == [0] * 24
+    assert d["table_cache"] == {"warmup_misses": 1, "warmup_hits": 23, "timed_misses": 0, "timed_hits": 48}
+    assert d["kernel"] == "rope_fast" and d["parity"]["mismatching_elements"] == 0
