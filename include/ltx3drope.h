@@ -259,7 +259,9 @@ int ltx3drope_apply_qk_shard(void* q_out, void* k_out, const void* q, const void
  * 2^31 or more), NOT_DEVICE_PTR,
  * TABLE_DEVICE (pointers on different devices), EXTENT.  can_use accepts
  * q_out and k_out both NULL (fresh outputs: only the inputs are checked);
- * apply_qk needs both.  apply_qk returns
+ * apply_qk needs both.  tokens = 0 is an empty call: the other sizes and the
+ * dtypes are checked, no pointer is looked at (an empty tensor's may be NULL),
+ * can_use returns 1 and apply_qk returns OK without launching.  apply_qk returns
  * E_UNSUPPORTED for any of these; the first call on a device allocates the
  * device's 256-byte counter (E_NOMEM when out of memory, E_HIP for another
  * HIP failure), and a failed launch gives E_HIP.
@@ -284,8 +286,10 @@ int ltx3drope_neox_position_errors(int device, int reset, int64_t* count);
  * i.e. channels packed as (channel, width offset, height offset).  Both tensors
  * contiguous, elements of elem_bytes = 1, 2, 4 or 8 bytes (the op moves data
  * and never looks at values, so it is exact for every dtype).  B, C, F, H, W
- * are always the unpatched sizes.  E_INVALID: a size or p <= 0, H or W not a
- * multiple of p, elem_bytes not 1/2/4/8, NULL pointers.  E_UNSUPPORTED: 2^32
+ * are always the unpatched sizes.  A size of 0 is an empty call: OK, nothing
+ * launched, no pointer looked at (an empty tensor's may be NULL).  E_INVALID:
+ * a size < 0, p <= 0, H or W not a multiple of p, elem_bytes not 1/2/4/8,
+ * NULL pointers of a non-empty call.  E_UNSUPPORTED: 2^32
  * elements or more (or C*p*p of 2^31 or more), pointers not aligned to one
  * element, overlapping tensors,
  * not device memory of one device, or allocations smaller than the tensors.

@@ -391,6 +391,18 @@ int apply_impl(void* q_out, void* k_out, const void* q, const void* k, int dtype
 int neox_precheck(const void* q_out, const void* k_out, const void* q, const void* k, int dtype, int64_t tokens,
                   int64_t q_heads, int64_t k_heads, int64_t D, const int64_t* positions, const void* cache,
                   int cache_dtype, int64_t max_position, bool check_memory, bool check_outputs, int* device_out) {
+    if (tokens == 0) {
+        // nothing to rotate: the sizes and dtypes must still be valid, no pointer is looked at
+        // (an empty tensor may have a null data pointer)
+        for (int d : {dtype, cache_dtype})
+            if (d != LTX3DROPE_DTYPE_F32 && d != LTX3DROPE_DTYPE_BF16) return LTX3DROPE_REASON_DTYPE;
+        if (q_heads <= 0 || k_heads <= 0 || D <= 0 || max_position <= 0) return LTX3DROPE_REASON_NONPOSITIVE_DIM;
+        if (D % 2) return LTX3DROPE_REASON_SPLIT_ODD;
+        if (q_heads >= (int64_t(1) << 31) || k_heads >= (int64_t(1) << 31) || D >= (int64_t(1) << 31) ||
+            max_position >= (int64_t(1) << 31) || max_position * D >= (int64_t(1) << 32))
+            return LTX3DROPE_REASON_TOO_LARGE;
+        return LTX3DROPE_REASON_OK;
+    }
     if ((check_outputs && (!q_out || !k_out)) || !q || !k || !positions || !cache) return LTX3DROPE_REASON_NULLPTR;
     for (int d : {dtype, cache_dtype})
         if (d != LTX3DROPE_DTYPE_F32 && d != LTX3DROPE_DTYPE_BF16) return LTX3DROPE_REASON_DTYPE;
@@ -585,6 +597,7 @@ int ltx3drope_neox_apply_qk(void* q_out, void* k_out, const void* q, const void*
         stats().rejected.fetch_add(1);
         return LTX3DROPE_E_UNSUPPORTED;
     }
+    if (tokens == 0) return LTX3DROPE_OK;  // nothing launched
     DeviceGuard guard(device);
     DeviceRes* res = nullptr;
     const int st = device_res(device, &res);
@@ -641,9 +654,11 @@ namespace {
 
 int patch_call(void* dst, const void* src, int elem_bytes, int64_t B, int64_t C, int64_t F, int64_t H, int64_t W,
                int64_t p, void* stream_ptr, bool inverse) {
-    if (!dst || !src) return LTX3DROPE_E_INVALID;
     if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return LTX3DROPE_E_INVALID;
-    if (B <= 0 || C <= 0 || F <= 0 || H <= 0 || W <= 0 || p <= 0 || H % p || W % p) return LTX3DROPE_E_INVALID;
+    if (B < 0 || C < 0 || F < 0 || H < 0 || W < 0 || p <= 0 || H % p || W % p) return LTX3DROPE_E_INVALID;
+    // an empty tensor: nothing to move, no pointer is looked at (it may be null)
+    if (B == 0 || C == 0 || F == 0 || H == 0 || W == 0) return LTX3DROPE_OK;
+    if (!dst || !src) return LTX3DROPE_E_INVALID;
     // fewer than 2^32 elements (the LDS kernels index 16-byte vectors with 32 bits), each size and
     // the packed channel count C*p*p below 2^31
     const int64_t lim = int64_t(1) << 32, size_lim = int64_t(1) << 31;

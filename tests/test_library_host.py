@@ -466,7 +466,14 @@ def test_neox_precheck_rules():
     assert call_neox_can_use(*good[:9], None, *good[10:]) == (0, "NULLPTR")
     assert call_neox_can_use(*good[:4], 5, *good[5:]) == (0, "DTYPE")
     assert call_neox_can_use(*good[:11], 9, good[12]) == (0, "DTYPE")
-    assert call_neox_can_use(*good[:5], 0, *good[6:]) == (0, "NONPOSITIVE_DIM")
+    assert call_neox_can_use(*good[:5], -1, *good[6:]) == (0, "NONPOSITIVE_DIM")
+    # no tokens: an empty call, valid whenever the other sizes and the dtypes are (pointers unread)
+    assert call_neox_can_use(*good[:5], 0, *good[6:]) == (1, "OK")
+    assert call_neox_can_use(None, None, None, None, bf, 0, 4, 2, 64, None, None, f32, 128) == (1, "OK")
+    assert call_neox_can_use(None, None, None, None, bf, 0, 4, 2, 63, None, None, f32, 128) == (0, "SPLIT_ODD")
+    assert call_neox_can_use(None, None, None, None, bf, 0, 0, 2, 64, None, None, f32, 128) == (0, "NONPOSITIVE_DIM")
+    assert call_neox_can_use(None, None, None, None, bf, 0, 4, 2, 64, None, None, 7, 128) == (0, "DTYPE")
+    assert call_neox_can_use(None, None, None, None, bf, 0, 4, 2, 64, None, None, f32, 1 << 31) == (0, "TOO_LARGE")
     assert call_neox_can_use(*good[:12], 0) == (0, "NONPOSITIVE_DIM")
     assert call_neox_can_use(*good[:8], 63, *good[9:]) == (0, "SPLIT_ODD")
     assert call_neox_can_use(qo + 1, *good[1:]) == (0, "ALIGN")
@@ -544,3 +551,22 @@ def test_size_limit_is_2_to_the_32_elements_per_tensor():
         assert call_can_use(*args, (1, 1, 1, 1 << 20, 64, 64), tab.handle) == (0, "TOO_LARGE")
     with rla.tables_build(1, 1, 1, (2, 2, 2)) as tab:
         assert call_can_use(*args, (1 << 31, 1, 1, 1, 1, 6), tab.handle) == (0, "TOO_LARGE")
+
+
+def test_empty_calls_launch_nothing():
+    """Zero tokens (rotate-half RoPE) or a zero size (patchify) is a successful call that reads no
+    pointer and launches nothing; negative sizes stay invalid."""
+    bf, f32 = _lib.DTYPE_BF16, _lib.DTYPE_F32
+    before = rla.stats()
+    assert L.ltx3drope_neox_apply_qk(None, None, None, None, bf, 0, 4, 2, 64, None, None, f32, 128, None) == _lib.OK
+    assert L.ltx3drope_neox_apply_qk(None, None, None, None, bf, -1, 4, 2, 64, None, None, f32, 128,
+                                     None) == _lib.E_UNSUPPORTED
+    for fn in (L.ltx3drope_patchify, L.ltx3drope_unpatchify):
+        for sizes in ((0, 3, 5, 8, 8), (1, 0, 5, 8, 8), (1, 3, 0, 8, 8), (1, 3, 5, 0, 8), (1, 3, 5, 8, 0)):
+            assert fn(None, None, 2, *sizes, 2, None) == _lib.OK
+        assert fn(None, None, 2, 1, 3, 5, 8, -8, 2, None) == _lib.E_INVALID
+        assert fn(None, None, 2, 0, 3, 5, 8, 6, 4, None) == _lib.E_INVALID  # W not a multiple of p
+        assert fn(None, None, 3, 0, 3, 5, 8, 8, 2, None) == _lib.E_INVALID  # element size
+        assert fn(None, None, 2, 1, 3, 5, 8, 8, 2, None) == _lib.E_INVALID  # NULL pointers of a real call
+    after = rla.stats()
+    assert after["fast_launches"] == before["fast_launches"] and after["plain_launches"] == before["plain_launches"]

@@ -173,6 +173,19 @@ def test_precheck_refusals_on_device():
     assert rla.stats()["fast_launches"] == 0 and rla.stats()["plain_launches"] == 0
 
 
+def test_zero_tokens():
+    """An empty token batch: empty outputs, nothing launched, no position error counted."""
+    q = torch.empty((0, 4, 64), dtype=torch.bfloat16, device=DEV)
+    k = torch.empty((0, 2, 64), dtype=torch.bfloat16, device=DEV)
+    pos = torch.empty(0, dtype=torch.int64, device=DEV)
+    cache = torch.zeros((16, 64), dtype=torch.float32, device=DEV)
+    assert rla.neox_can_use(q, k, pos, cache) == (True, "OK")
+    qo, ko = rla.neox_apply_qk(q, k, pos, cache)
+    assert qo.shape == q.shape and ko.shape == k.shape
+    assert rla.stats()["fast_launches"] == 0 and rla.stats()["plain_launches"] == 0
+    assert rla.neox_position_errors(0) == 0
+
+
 @pytest.mark.parametrize("seed", [11, 22])
 def test_random_configurations(seed):
     """Twenty seeded random configurations per seed (head_dim, head counts, dtypes, cache sizes; half

@@ -91,12 +91,23 @@ def test_refusals():
     L = _lib.lib()
     y = torch.empty((1, 8, 1, 4, 4), dtype=torch.bfloat16, device=DEV)
     assert L.ltx3drope_patchify(y.data_ptr(), x.data_ptr(), 3, 1, 2, 1, 8, 8, 2, None) == _lib.E_INVALID
-    assert L.ltx3drope_patchify(y.data_ptr(), x.data_ptr(), 2, 1, 2, 1, 8, 0, 2, None) == _lib.E_INVALID
+    assert L.ltx3drope_patchify(y.data_ptr(), x.data_ptr(), 2, 1, 2, 1, 8, -8, 2, None) == _lib.E_INVALID
     assert L.ltx3drope_patchify(x.data_ptr() + 2, x.data_ptr(), 2, 1, 2, 1, 8, 8, 2, None) == _lib.E_UNSUPPORTED
     small = torch.empty(16, dtype=torch.bfloat16, device=DEV)
     assert L.ltx3drope_patchify(y.data_ptr(), small.data_ptr(), 2, 1, 2, 1, 800, 800, 2, None) == _lib.E_UNSUPPORTED
     host = torch.zeros((1, 2, 1, 8, 8), dtype=torch.bfloat16).pin_memory()
     assert L.ltx3drope_patchify(y.data_ptr(), host.data_ptr(), 2, 1, 2, 1, 8, 8, 2, None) == _lib.E_UNSUPPORTED
+    assert rla.stats()["fast_launches"] == 0 and rla.stats()["plain_launches"] == 0
+
+
+def test_empty_tensors():
+    """An empty batch (or frame count) gives an empty result of the right shape; nothing launches."""
+    for shape in ((0, 3, 5, 8, 8), (2, 3, 0, 8, 8)):
+        x = torch.empty(shape, dtype=torch.bfloat16, device=DEV)
+        y = rla.patchify(x, 4)
+        assert tuple(y.shape) == (shape[0], 48, shape[2], 2, 2)
+        back = rla.unpatchify(y, 4)
+        assert tuple(back.shape) == shape
     assert rla.stats()["fast_launches"] == 0 and rla.stats()["plain_launches"] == 0
 
 
