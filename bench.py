@@ -14,9 +14,12 @@ Printed: one JSON line.  value = algorithmic bytes per step / wall time per step
 (GB/s).  roofline.achieved = algorithmic bytes per launch / the kernel's average
 duration: the time between two HIP events recorded on the kernel's stream before
 the first and after the last of the K timed launches, divided by K (the launches
-run back to back; no marker sits between two kernels).  cpu_baseline = the CPU
-oracle timed on the host on a bounded slab of the same workload, scaled to the
-same unit.
+run back to back; no marker sits between two kernels).  The CPU leg (the
+cpu_leg_* functions, the only code here that runs the oracle, which is test
+infrastructure) computes the oracle's result on a bounded sample of the same
+workload: the GPU's timed outputs are compared with it element by element
+(parity), and the oracle's time on the host over a longer sample, scaled to the
+same unit, is cpu_baseline (skipped with --no-cpu-baseline).
 
 --op neox | patchify | unpatchify time the secondary kernels the same way
 (200 warm-up and 200 timed launches of about 0.13 ms each by default), with
@@ -308,33 +311,10 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, kernel avg {kavg_s * 1e6:.1f} us, "
           f"{achieved:.0f} GB/s kernel", file=sys.stderr, flush=True)
 
-    # parity of the timed output on sampled tokens (the oracle computes them one by one)
-    import oracle
-
-    ids = workloads.sample_tokens(B * T * H * W, 256, seed=1234)
-    idx = torch.from_numpy(ids).to(dev)
-    mism = 0
     if not args.inplace:
         assert torch.equal(sets[last_in][0], q) and torch.equal(sets[last_in][1], k)
-    for x_np, out in ((q_np, qo), (k_np, ko)):
-        if args.inplace:
-            # the sampled rows after as many in-place rotations as this input set received
-            tabs = oracle.grid_tables(T, H, W, w.split, w.base)
-            coords = oracle.token_coords(ids, T, H, W)
-            want = x_np.reshape(B * T * H * W, heads, D)[ids]
-            for _ in range(applied[last_in]):
-                want = oracle.apply_rope_tokens(want, w.dtype, coords, tabs, w.split)
-        else:
-            want = oracle.rope3d_sampled(x_np, w.dtype, w.split, ids, w.base)
-        got = out.view(B * T * H * W, heads, D)[idx].cpu()
-        got = got.view(torch.int16).numpy().view(np.uint16) if es == 2 else got.numpy()
-        mism += int((got.view(want.dtype) != want).sum())
-
     copy_gbs = copy_ceiling(sets, stream)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, gi, q_np, k_np, args.cpu_seconds, args.cpu_threads)
+    parity, cpu = cpu_leg_rope3d(w, gi, q_np, k_np, qo, ko, applied[last_in] if args.inplace else 0, args)
 
     traffic = measured_traffic(w.name)
     line = {
@@ -361,14 +341,14 @@ def main():
         "kernel_avg_us": round(kavg_s * 1e6, 2),
         "timed_region_device_allocations": new_segments,
         "copy_ceiling_GBps": None if copy_gbs is None else round(copy_gbs, 1),
-        "parity": {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0},
+        "parity": parity,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
-    if mism:
+    if parity["mismatching_elements"]:
         sys.exit(1)
 
 
@@ -379,7 +359,6 @@ def main_cycle(args):
     import numpy as np
     import torch
 
-    import oracle
     import rope_ltx3drope_amd as rla
     import workloads
 
@@ -442,18 +421,11 @@ def main_cycle(args):
     achieved = alg_pass * args.steps / gpu_s / 1e9
     value = alg_pass / (wall / args.steps) / 1e9
 
-    # parity: sampled tokens of every grid's last outputs against the oracle
-    mism, sampled = 0, 0
-    for gi, (q_np, k_np) in zip(grids, host):
-        B, T, H, W, heads, D = w.shape(gi)
-        ids = workloads.sample_tokens(B * T * H * W, 128, seed=4321 + gi)
-        idx = torch.from_numpy(ids).to(dev)
-        for x_np, out in ((q_np, last[gi][0]), (k_np, last[gi][1])):
-            want = oracle.rope3d_sampled(x_np, w.dtype, w.split, ids, w.base)
-            got = out.view(B * T * H * W, heads, D)[idx].cpu()
-            got = got.view(torch.int16).numpy().view(np.uint16) if w.itemsize == 2 else got.numpy()
-            mism += int((got.view(want.dtype) != want).sum())
-        sampled += len(ids)
+    parity = {"sampled_tokens": 0, "mismatching_elements": 0, "tolerance_ulp": 0}
+    for gi, (q_np, k_np) in zip(grids, host):  # every grid's last outputs
+        pg, _ = cpu_leg_rope3d(w, gi, q_np, k_np, *last[gi], 0, args, count=128, seed=4321 + gi, time_it=False)
+        parity["sampled_tokens"] += pg["sampled_tokens"]
+        parity["mismatching_elements"] += pg["mismatching_elements"]
     copy_gbs = copy_ceiling([inputs[grids[0]]], stream)
     line = {
         "metric": METRIC,
@@ -482,13 +454,13 @@ def main_cycle(args):
                         "timed_misses": st["cache_misses"] - warm["cache_misses"],
                         "timed_hits": st["cache_hits"] - warm["cache_hits"]},
         "copy_ceiling_GBps": round(copy_gbs, 1),
-        "parity": {"sampled_tokens": sampled, "mismatching_elements": mism, "tolerance_ulp": 0},
+        "parity": parity,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
-    if mism:
+    if parity["mismatching_elements"]:
         sys.exit(1)
 
 
@@ -497,7 +469,6 @@ def main_neox(args):
     import numpy as np
     import torch
 
-    import oracle.neox as nx
     import rope_ltx3drope_amd as rla
     import workloads
 
@@ -548,19 +519,11 @@ def main_neox(args):
     wall = time.perf_counter() - t0
     kavg = e0.elapsed_time(e1) / args.steps / 1e3  # launches run back to back: no marker between them
     qo, ko = outs[-1]
-    ids = workloads.sample_tokens(w.tokens, 256, seed=99)
-    idx = torch.from_numpy(ids).to(dev)
-    mism = 0
-    for x_np, out in ((q_np, qo), (k_np, ko)):
-        want = nx.neox_rope(x_np[ids], w.dtype, pos_np[ids], cache_np, w.cache_dtype)
-        got = out[idx].cpu()
-        got = got.view(torch.int16).numpy().view(np.uint16) if w.dtype == workloads.BF16 else got.numpy()
-        mism += int((got.view(want.dtype) != want).sum())
     st = rla.stats()
     kernel = "neox_fast" if st["fast_launches"] else "neox_plain"
     del outs
     copy_gbs = copy_ceiling(sets, stream)
-    cpu = None if args.no_cpu_baseline else neox_cpu_baseline(w, q_np, k_np, pos_np, cache_np, args.cpu_seconds)
+    parity, cpu = cpu_leg_neox(w, q_np, k_np, pos_np, cache_np, qo, ko, args)
     line = {
         "metric": "rotate-half RoPE with gathered cos/sin cache, achieved HBM GB/s, bit-exact vs oracle",
         "value": round(alg / (wall / args.steps) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -574,14 +537,14 @@ def main_neox(args):
         "kernel_avg_us": round(kavg * 1e6, 2),
         "timed_region_device_allocations": new_segments,
         "copy_ceiling_GBps": round(copy_gbs, 1),
-        "parity": {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0},
+        "parity": parity,
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.key, kernel)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
-    if mism:
+    if parity["mismatching_elements"]:
         sys.exit(1)
 
 
@@ -592,7 +555,6 @@ def main_dit(args):
     import numpy as np
     import torch
 
-    import oracle.dit_freqs as df
     import rope_ltx3drope_amd as rla
 
     dev = torch.device("cuda:0")
@@ -606,14 +568,8 @@ def main_dit(args):
         for _ in range(args.steps):
             out = rla.dit_freq_grid(theta, dim, ne, double, device=dev)
         per_call["f64" if double else "f32"] = (time.perf_counter() - t0) / args.steps
-        want = df.freq_grid(theta, dim, ne, double)
-        mism += int((out.cpu().numpy().view(np.uint32) != want.view(np.uint32)).sum())
-    t0 = time.perf_counter()
-    reps = 0
-    while time.perf_counter() - t0 < 1.0:
-        df.freq_grid(theta, dim, ne, True)
-        reps += 1
-    oracle_us = (time.perf_counter() - t0) / reps * 1e6
+        mism += cpu_leg_dit(theta, dim, ne, double, out.cpu().numpy())
+    oracle_us = cpu_leg_dit_time(theta, dim, ne)
     us = per_call["f64"] * 1e6
     line = {
         "metric": "LTX DiT RoPE frequency grid delivered to the device, time per call, bit-exact vs oracle",
@@ -645,7 +601,6 @@ def main_patch(args):
     import numpy as np
     import torch
 
-    import oracle.patchify as pf
     import rope_ltx3drope_amd as rla
     import workloads
 
@@ -699,33 +654,7 @@ def main_patch(args):
     del outs
     copy_gbs = copy_ceiling([(t,) for t in sets], stream)
     del sets
-    # the oracle on the whole workload: the parity reference for patchify and, repeated on one core
-    # for about --cpu-seconds, the CPU baseline of either direction
-    if inverse:
-        want = x_np
-        fn_cpu, src_cpu = pf.unpatchify, None if args.no_cpu_baseline else pf.patchify(x_np, p)
-    else:
-        fn_cpu, src_cpu = pf.patchify, x_np
-    cpu, calls, cpu_s = None, 0, 0.0
-    if not args.no_cpu_baseline:
-        pin_one_core()
-    while src_cpu is not None:
-        t0 = time.perf_counter()
-        res = fn_cpu(src_cpu, p)
-        cpu_s += time.perf_counter() - t0
-        calls += 1
-        if not inverse and calls == 1:
-            want = res
-        del res
-        if args.no_cpu_baseline or cpu_s >= args.cpu_seconds:
-            break
-    del src_cpu
-    if not args.no_cpu_baseline:
-        cpu = {"value": round(calls * alg / cpu_s / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "seconds": round(cpu_s, 2),
-               "sample": f"the whole workload, {calls} {args.op} calls; numpy, one thread pinned to one core; "
-                         f"CPU: {_cpu_model()}"}
-    mism = int((got != want).sum())
+    parity, cpu = cpu_leg_patch(x_np, p, inverse, got, alg, args)
     st = rla.stats()
     kernel = patch_kernel_name(st["fast_launches"] > 0, inverse)
     name = patch_workload_name(args.op, shape, p, eb)
@@ -742,13 +671,13 @@ def main_patch(args):
         "kernel_avg_us": round(kavg * 1e6, 2),
         "timed_region_device_allocations": new_segments,
         "copy_ceiling_GBps": round(copy_gbs, 1),
-        "parity": {"compared_elements": int(got.size), "mismatching_elements": mism, "tolerance_ulp": 0},
+        "parity": parity,
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, kernel)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
-    if mism:
+    if parity["mismatching_elements"]:
         sys.exit(1)
 
 
@@ -798,6 +727,125 @@ def copy_ceiling(sets, stream, reps_per_set: int = 10) -> float:
 def patch_workload_name(op: str, shape, p: int, elem_bytes: int) -> str:
     dt = {1: "u8", 2: "bf16", 4: "f32", 8: "u64"}[elem_bytes]
     return f"{op}_{dt}_{'x'.join(str(d) for d in shape)}_p{p}"
+
+
+# ---------------------------------------------------------------------------
+# The CPU leg: the only code in this file that runs the oracle (test infrastructure).  It
+# computes the oracle's result on a bounded sample of the workload, compares the GPU's timed
+# outputs with it element by element (the line's "parity"), and, unless --no-cpu-baseline, times
+# the oracle on the host cores over a longer sample (the line's "cpu_baseline").
+# ---------------------------------------------------------------------------
+
+def cpu_leg_rope3d(w, gi, q_np, k_np, qo, ko, rotations, args, count=256, seed=1234, time_it=True):
+    """3D RoPE: the oracle on `count` sampled tokens of grid `gi` against the GPU outputs qo, ko
+    (rotations > 0: in-place mode, the oracle applied that many times to the input rows), then
+    the timed oracle on whole (batch, frame) slabs.  Returns (parity, cpu_baseline or None)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    B, T, H, W, heads, D = w.shape(gi)
+    ids = workloads.sample_tokens(B * T * H * W, count, seed=seed)
+    idx = torch.from_numpy(ids).to(qo.device)
+    mism = 0
+    for x_np, out in ((q_np, qo), (k_np, ko)):
+        if rotations:
+            tabs = oracle.grid_tables(T, H, W, w.split, w.base)
+            coords = oracle.token_coords(ids, T, H, W)
+            want = x_np.reshape(B * T * H * W, heads, D)[ids]
+            for _ in range(rotations):
+                want = oracle.apply_rope_tokens(want, w.dtype, coords, tabs, w.split)
+        else:
+            want = oracle.rope3d_sampled(x_np, w.dtype, w.split, ids, w.base)
+        got = out.view(B * T * H * W, heads, D)[idx].cpu()
+        got = got.view(torch.int16).numpy().view(np.uint16) if w.itemsize == 2 else got.numpy()
+        mism += int((got.view(want.dtype) != want).sum())
+    parity = {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0}
+    cpu = None
+    if time_it and not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, gi, q_np, k_np, args.cpu_seconds, args.cpu_threads)
+    return parity, cpu
+
+
+def cpu_leg_neox(w, q_np, k_np, pos_np, cache_np, qo, ko, args):
+    """Rotate-half RoPE: the oracle on 256 sampled tokens against the GPU outputs, then the timed
+    oracle on consecutive chunks.  Returns (parity, cpu_baseline or None)."""
+    import numpy as np
+    import torch
+
+    import oracle.neox as nx
+    import workloads
+
+    ids = workloads.sample_tokens(w.tokens, 256, seed=99)
+    idx = torch.from_numpy(ids).to(qo.device)
+    mism = 0
+    for x_np, out in ((q_np, qo), (k_np, ko)):
+        want = nx.neox_rope(x_np[ids], w.dtype, pos_np[ids], cache_np, w.cache_dtype)
+        got = out[idx].cpu()
+        got = got.view(torch.int16).numpy().view(np.uint16) if w.dtype == workloads.BF16 else got.numpy()
+        mism += int((got.view(want.dtype) != want).sum())
+    parity = {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0}
+    cpu = None if args.no_cpu_baseline else neox_cpu_baseline(w, q_np, k_np, pos_np, cache_np, args.cpu_seconds)
+    return parity, cpu
+
+
+def cpu_leg_dit(theta, dim, ne, double, got) -> int:
+    """DiT frequency grid: elements of the GPU's grid that differ from the oracle's, bit for bit."""
+    import numpy as np
+
+    import oracle.dit_freqs as df
+
+    want = df.freq_grid(theta, dim, ne, double)
+    return int((got.view(np.uint32) != want.view(np.uint32)).sum())
+
+
+def cpu_leg_dit_time(theta, dim, ne) -> float:
+    """The oracle's float64 recipe, repeated for about a second: microseconds per call."""
+    import oracle.dit_freqs as df
+
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < 1.0:
+        df.freq_grid(theta, dim, ne, True)
+        reps += 1
+    return (time.perf_counter() - t0) / reps * 1e6
+
+
+def cpu_leg_patch(x_np, p, inverse, got, alg, args):
+    """patchify / unpatchify: the oracle on the whole workload, compared element by element with
+    the GPU's output; then, unless --no-cpu-baseline, the same call repeated on one core for about
+    --cpu-seconds.  Returns (parity, cpu_baseline or None)."""
+    import oracle.patchify as pf
+
+    if inverse:
+        want = x_np
+        fn_cpu, src_cpu = pf.unpatchify, None if args.no_cpu_baseline else pf.patchify(x_np, p)
+    else:
+        fn_cpu, src_cpu = pf.patchify, x_np
+    cpu, calls, cpu_s = None, 0, 0.0
+    if not args.no_cpu_baseline:
+        pin_one_core()
+    while src_cpu is not None:
+        t0 = time.perf_counter()
+        res = fn_cpu(src_cpu, p)
+        cpu_s += time.perf_counter() - t0
+        calls += 1
+        if not inverse and calls == 1:
+            want = res
+        del res
+        if args.no_cpu_baseline or cpu_s >= args.cpu_seconds:
+            break
+    del src_cpu
+    if not args.no_cpu_baseline:
+        cpu = {"value": round(calls * alg / cpu_s / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "seconds": round(cpu_s, 2),
+               "sample": f"the whole workload, {calls} {args.op} calls; numpy, one thread pinned to one core; "
+                         f"CPU: {_cpu_model()}"}
+    parity = {"compared_elements": int(got.size), "mismatching_elements": int((got != want).sum()),
+              "tolerance_ulp": 0}
+    return parity, cpu
 
 
 def neox_cpu_baseline(w, q_np, k_np, pos_np, cache_np, target_s):

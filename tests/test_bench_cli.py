@@ -98,3 +98,23 @@ def test_cycle_mode_refuses_other_rope_options(monkeypatch, extra):
     with pytest.raises(SystemExit) as e:
         bench.main()
     assert "--cycle" in str(e.value.code)
+
+
+def test_only_the_cpu_leg_runs_the_oracle():
+    """bench.py imports the oracle (test infrastructure) only inside its CPU leg: the cpu_leg_*
+    functions and the baseline timers they call."""
+    import ast
+
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    allowed = {"cpu_baseline", "neox_cpu_baseline"}
+    for fn in [n for n in tree.body if isinstance(n, ast.FunctionDef)]:
+        for node in ast.walk(fn):
+            names = []
+            if isinstance(node, ast.Import):
+                names = [a.name for a in node.names]
+            elif isinstance(node, ast.ImportFrom):
+                names = [node.module or ""]
+            if any(n == "oracle" or n.startswith("oracle.") for n in names):
+                assert fn.name.startswith("cpu_leg_") or fn.name in allowed, fn.name
+    top = [n for n in tree.body if isinstance(n, (ast.Import, ast.ImportFrom))]
+    assert not any("oracle" in ast.dump(n) for n in top)
