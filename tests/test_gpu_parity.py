@@ -194,6 +194,44 @@ def test_random_configurations(seed):
     assert rla.stats()["gate_disabled"] == 0
 
 
+def _random_wide_configs(n, seed):
+    """Seeded random configurations with wide token rows (up to 40 heads, head_dim up to 192) on
+    small grids: rows of whole wavefronts (one decode per wavefront, the token's table row in LDS),
+    rows of 32+ vectors that span tokens, and short rows, with aligned and arbitrary even splits."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dtype = oracle.BF16 if rng.random() < 0.6 else oracle.F32
+        step = (8 if dtype == oracle.BF16 else 4) if rng.random() < 0.5 else 2
+        split = tuple(int(step * rng.integers(1, 64 // step + 1)) for _ in range(3))
+        heads = int(rng.choice([1, 3, 4, 8, 12, 16, 24, 32, 40]))
+        shape = (int(rng.integers(1, 3)), int(rng.integers(1, 5)), int(rng.integers(1, 5)), int(rng.integers(1, 5)),
+                 heads, sum(split))
+        offsets = (0, 0, 0) if rng.random() < 0.6 else tuple(int(x) for x in rng.integers(0, 3, 3))
+        out.append((shape, split, dtype, offsets))
+    return out
+
+
+@pytest.mark.parametrize("seed", [404, 505])
+def test_random_wide_rows(seed):
+    """Twelve wide-row random configurations per seed, through the gate and the plain kernel,
+    element by element against the oracle."""
+    for shape, split, dtype, offsets in _random_wide_configs(12, seed):
+        log(f"wide {shape} {split} {dtype} offsets {offsets}")
+        q, k = workloads.generate_custom(shape, dtype, seed=seed + sum(shape))
+        grid = tuple(n + o for n, o in zip(shape[1:4], offsets))
+        want_q, want_k = oracle.rope3d_qk(q, k, dtype, split, 10000.0, offsets=offsets, grid=grid)
+        dq, dk = to_dev(q, dtype), to_dev(k, dtype)
+        for path in (0, 2):
+            rla.set_option(rla.OPT_PATH, path)
+            qo, ko = rla.forward_pair(dq, dk, split, 10000.0, grid=grid,
+                                      offsets=None if offsets == (0, 0, 0) else offsets)
+            torch.cuda.synchronize()
+            assert_bitexact(to_host(qo, dtype), want_q, dtype, f"q {shape} {split} path {path}")
+            assert_bitexact(to_host(ko, dtype), want_k, dtype, f"k {shape} {split} path {path}")
+    assert rla.stats()["gate_disabled"] == 0
+
+
 def test_misaligned_views_use_plain_kernel():
     shape, split = (1, 3, 4, 5, 4, 32), (8, 8, 16)
     q, k = workloads.generate_custom(shape, oracle.BF16, seed=5)
