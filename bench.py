@@ -24,8 +24,7 @@ same unit, is cpu_baseline (skipped with --no-cpu-baseline).
 --op neox | patchify | unpatchify time the secondary kernels the same way
 (200 warm-up and 200 timed launches of about 0.13 ms each by default), with
 their own counter records and CPU-oracle baselines.
---op dit_freqs times the host-built DiT frequency grid delivered to the device
-(no kernel: float64 host math, one upload; roofline null).
+--op dit_freqs times the DiT frequency-grid kernel (launch-bound: roofline null).
 """
 from __future__ import annotations
 
@@ -549,40 +548,51 @@ def main_neox(args):
 
 
 def main_dit(args):
-    """LTX DiT RoPE frequency grid (theta 10000, dim 4096, 6 rope elements: 682 values) built on the
-    host and delivered to the device, float64 and float32 recipes: time per call (each call ends
-    with the copy to the device complete), bit-exact against the oracle."""
+    """LTX DiT RoPE frequency grid (theta 10000, dim 4096, 6 rope elements: 682 values) generated on
+    the device by one kernel launch per call, float64 and float32 recipes: kernel time per call from
+    two events around the K back-to-back launches, bit-exact against the oracle."""
     import numpy as np
     import torch
 
     import rope_ltx3drope_amd as rla
 
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
     theta, dim, ne = 10000.0, 4096, 6
-    per_call, mism = {}, 0
+    per_call, wall_call, mism = {}, {}, 0
     for double in (True, False):
         for _ in range(args.warmup):
             rla.dit_freq_grid(theta, dim, ne, double, device=dev)
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record(stream)
         for _ in range(args.steps):
             out = rla.dit_freq_grid(theta, dim, ne, double, device=dev)
-        per_call["f64" if double else "f32"] = (time.perf_counter() - t0) / args.steps
+        e1.record(stream)
+        torch.cuda.synchronize()
+        key = "f64" if double else "f32"
+        wall_call[key] = (time.perf_counter() - t0) / args.steps
+        per_call[key] = e0.elapsed_time(e1) / 1e3 / args.steps
         mism += cpu_leg_dit(theta, dim, ne, double, out.cpu().numpy())
     oracle_us = cpu_leg_dit_time(theta, dim, ne)
     us = per_call["f64"] * 1e6
     line = {
-        "metric": "LTX DiT RoPE frequency grid delivered to the device, time per call, bit-exact vs oracle",
-        "value": round(us, 2), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(us / 1e3, 5), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f64", "data": "synthetic (fixed parameters)",
+        "metric": "LTX DiT RoPE frequency grid generated on the device, time per call, bit-exact vs oracle",
+        "value": round(us, 3), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall_call["f64"] * 1e3, 5), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic (fixed parameters)",
         "config": {"workload": "dit_freqs_theta1e4_dim4096_ne6", "values": dim // ne,
-                   "f32_recipe_us": round(per_call["f32"] * 1e6, 2)},
-        "kernel": None, "parity": {"compared_elements": 2 * (dim // ne), "mismatching_elements": mism,
-                                   "tolerance_ulp": 0},
+                   "f32_recipe_kernel_us": round(per_call["f32"] * 1e6, 3),
+                   "f32_recipe_wall_us": round(wall_call["f32"] * 1e6, 2)},
+        "kernel": "dit_freqs", "kernel_avg_us": round(us, 3),
+        "parity": {"compared_elements": 2 * (dim // ne), "mismatching_elements": mism, "tolerance_ulp": 0},
         "roofline": None,
+        "roofline_note": "682 values in 3 workgroups of one launch: bound by launch latency, not by HBM or "
+                         "arithmetic throughput",
         "cpu_baseline": {"value": round(oracle_us, 2), "unit": "us", "cores": 1, "kind": "oracle",
-                         "sample": "the float64 recipe, host array only"},
+                         "sample": "the float64 recipe, one whole grid per call (exact rationals and 60-digit "
+                                   "decimals)"},
     }
     print(json.dumps(line), flush=True)
     if mism:
@@ -802,7 +812,8 @@ def cpu_leg_dit(theta, dim, ne, double, got) -> int:
 
 
 def cpu_leg_dit_time(theta, dim, ne) -> float:
-    """The oracle's float64 recipe, repeated for about a second: microseconds per call."""
+    """The oracle's float64 recipe, repeated for about a second (at least once): microseconds per
+    call."""
     import oracle.dit_freqs as df
 
     t0 = time.perf_counter()

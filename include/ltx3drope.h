@@ -303,21 +303,27 @@ int ltx3drope_unpatchify(void* x, const void* y, int elem_bytes, int64_t B, int6
                          int64_t W, int64_t p, void* stream);
 
 /*
- * LTX DiT RoPE frequency grid (sglang PR #24660 page, "Key source snippets",
- * the DiT's frequency generation; "Implementation breakdown", step 2):
+ * LTX DiT RoPE frequency grid, generated on the device (sglang PR #24660 page,
+ * "Key source snippets", the DiT's frequency generation; "Implementation
+ * breakdown", step 2: generated on the target device in the requested
+ * precision, keeping the official rounding trajectory):
  *     n = dim / num_rope_elems (integer division)
  *     out[i] = float32( theta ** linspace(0, 1, n)[i] * pi / 2 )
- * computed in float64 (double_precision = 1) or float32 (0).  linspace holds
- * i / (n - 1) correctly rounded to the working dtype (0 for n = 1); in float32
- * theta, the power and pi are each rounded to float32 and the product is an
- * fp32 product.  Built on the host (libm); written to `out`, n floats, which is
- * device memory when out_on_device = 1 (uploaded on `stream`, then that stream
- * is synchronized) and host memory otherwise.  *count (if not NULL) receives n.
- * E_INVALID: theta not finite or <= 0, dim < 0, num_rope_elems <= 0, n > 2^24,
- * out NULL while n > 0.  E_HIP, E_NOMEM.
+ * in float64 (double_precision = 1) or float32 (0), every step rounded to
+ * nearest even in that precision: linspace as torch.linspace computes it (a
+ * rounded step s = 1/(n-1); s*i for i < n/2, else 1 - s*(n-1-i) rounded once),
+ * the correctly rounded power (theta first rounded to float32 in the float32
+ * recipe), pi rounded to the working precision, an exact halving, and in the
+ * float64 recipe one rounding to float32 at the end.
+ * `out`: device memory of n floats (written by one kernel launch on `stream`,
+ * asynchronous; its device is the current one).  *count (if not NULL) receives
+ * n; n = 0 launches nothing and `out` may be NULL.
+ * E_INVALID: theta not in [2^-126, FLT_MAX] (a normal float32), dim < 0,
+ * num_rope_elems <= 0, n > 2^24, out NULL while n > 0.  E_UNSUPPORTED: `out`
+ * is not device memory holding n floats.  E_HIP: the launch failed.
  */
 int ltx3drope_dit_freq_grid(double theta, int64_t dim, int64_t num_rope_elems, int double_precision, float* out,
-                            int out_on_device, void* stream, int64_t* count);
+                            void* stream, int64_t* count);
 
 /* Gate state of one configuration key (LTX3DROPE_GATE_*), or a negative status. */
 int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W,

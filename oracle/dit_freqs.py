@@ -44,7 +44,13 @@ _PREC = 60  # decimal digits of the power before its one rounding
 
 
 def round_to(v: Fraction, double: bool):
-    """v rounded to nearest, ties to even, in float64 (double) or float32."""
+    """v rounded to nearest, ties to even, in float64 (double) or float32.  Magnitudes from halfway
+    between the largest finite value and the next power of two upward round to infinity (IEEE
+    overflow under round to nearest)."""
+    emax, mant = (1024, 53) if double else (128, 24)
+    if abs(v) >= Fraction(2) ** emax - Fraction(2) ** (emax - mant - 1):
+        inf = np.float64(np.inf) if double else np.float32(np.inf)
+        return inf if v > 0 else -inf
     if double:
         return np.float64(v.numerator / v.denominator)  # Python's int division rounds correctly
     g = np.float32(v.numerator / v.denominator)  # within one float32 step of the answer
@@ -103,6 +109,13 @@ def pow_rn(base: float, x: float, double: bool):
     return r
 
 
+def _halved_f32(prod) -> np.float32:
+    """prod / 2 (exact) rounded to float32; an overflowed product stays infinite."""
+    if math.isinf(float(prod)):
+        return np.float32(prod)
+    return round_to(Fraction(float(prod)) / 2, False)
+
+
 def freq_grid(theta: float, dim: int, num_rope_elems: int, double_precision: bool) -> np.ndarray:
     """The float32 grid of dim // num_rope_elems frequencies, float64 or float32 recipe."""
     n = dim // num_rope_elems
@@ -113,12 +126,12 @@ def freq_grid(theta: float, dim: int, num_rope_elems: int, double_precision: boo
         for i, xi in enumerate(x):
             p = pow_rn(theta, float(xi), True)
             prod = round_to(Fraction(float(p)) * pi, True)
-            out[i] = round_to(Fraction(float(prod)) / 2, False)
+            out[i] = _halved_f32(prod)
         return out
     th = float(np.float32(theta))
     pi = Fraction(float(np.float32(math.pi)))
     for i, xi in enumerate(x):
         p = pow_rn(th, float(xi), False)
         prod = round_to(Fraction(float(p)) * pi, False)
-        out[i] = round_to(Fraction(float(prod)) / 2, False)
+        out[i] = _halved_f32(prod)
     return out

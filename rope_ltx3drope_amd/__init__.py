@@ -377,25 +377,24 @@ def unpatchify(y, p: int, out=None, stream=None):
 
 
 def dit_freq_grid(theta: float, dim: int, num_rope_elems: int, double_precision: bool, device=None, stream=None):
-    """LTX DiT RoPE frequencies (float32, dim // num_rope_elems values): on `device` (a torch device)
-    when given, else as a numpy array."""
+    """LTX DiT RoPE frequencies (float32, dim // num_rope_elems values), generated by one kernel on
+    `device` (a torch device; default: the current one) and returned as a device tensor."""
+    L = _lib.lib()  # fails loudly when the library is missing, before any device is touched
+    torch = _torch()
     if int(num_rope_elems) <= 0:
         raise ValueError("num_rope_elems must be positive")
     count = max(0, int(dim) // int(num_rope_elems))
-    n = ctypes.c_int64(0)
-    args = (float(theta), int(dim), int(num_rope_elems), int(bool(double_precision)))
     if device is None:
-        import numpy as np
-
-        out = np.empty(count, np.float32)
-        ptr = out.ctypes.data_as(ctypes.c_void_p) if count else None
-        _check(_lib.lib().ltx3drope_dit_freq_grid(*args, ptr, 0, None, ctypes.byref(n)), "dit_freq_grid")
-        return out
-    torch = _torch()
+        device = torch.device("cuda", torch.cuda.current_device())
     out = torch.empty(count, dtype=torch.float32, device=device)
-    ptr = out.data_ptr() if count else None
-    _check(_lib.lib().ltx3drope_dit_freq_grid(*args, ptr, 1, _stream_ptr(out.device, stream), ctypes.byref(n)),
-           "dit_freq_grid")
+    if not out.is_cuda:
+        raise Ltx3dRopeUnsupported("NOT_DEVICE_PTR")
+    n = ctypes.c_int64(0)
+    st = L.ltx3drope_dit_freq_grid(float(theta), int(dim), int(num_rope_elems), int(bool(double_precision)),
+                                   out.data_ptr() if count else None, _stream_ptr(out.device, stream), ctypes.byref(n))
+    if st == _lib.E_UNSUPPORTED:
+        raise Ltx3dRopeUnsupported("NOT_DEVICE_PTR", st)
+    _check(st, "dit_freq_grid")
     return out
 
 

@@ -116,7 +116,7 @@ def lib() -> ctypes.CDLL:
             "ltx3drope_neox_position_errors": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.POINTER(i64)]),
             "ltx3drope_patchify": (ctypes.c_int, [vp, vp, ctypes.c_int] + [i64] * 6 + [vp]),
             "ltx3drope_unpatchify": (ctypes.c_int, [vp, vp, ctypes.c_int] + [i64] * 6 + [vp]),
-            "ltx3drope_dit_freq_grid": (ctypes.c_int, [ctypes.c_double, i64, i64, ctypes.c_int, vp, ctypes.c_int, vp,
+            "ltx3drope_dit_freq_grid": (ctypes.c_int, [ctypes.c_double, i64, i64, ctypes.c_int, vp, vp,
                                                        ctypes.POINTER(i64)]),
             "ltx3drope_gate_state": (ctypes.c_int, [ctypes.c_int, ctypes.c_int] + [i64] * 9),
             "ltx3drope_gate_reset": (ctypes.c_int, []),

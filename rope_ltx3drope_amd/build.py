@@ -36,6 +36,7 @@ SOURCES = [  # (file, language, extra flags)
     ("kernels.hip", "hip", DEVICE),
     ("neox.hip", "hip", DEVICE),
     ("patchify.hip", "hip", DEVICE),
+    ("dit_freqs.hip", "hip", DEVICE),
     ("api.cpp", "c++", ["-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include")]),
     ("tables.cpp", "c++", ["-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-fno-builtin"]),
 ]

@@ -731,6 +731,37 @@ int ltx3drope_unpatchify(void* x, const void* y, int elem_bytes, int64_t B, int6
     return patch_call(x, y, elem_bytes, B, C, F, H, W, p, stream, true);
 }
 
+int ltx3drope_dit_freq_grid(double theta, int64_t dim, int64_t num_rope_elems, int double_precision, float* out,
+                            void* stream, int64_t* count) {
+    // theta must be a normal float32 (the float32 recipe rounds it to one; a smaller or larger
+    // base would leave the power's domain this library covers)
+    if (!std::isfinite(theta) || theta < 0x1p-126 || theta > 0x1.fffffep+127 || dim < 0 || num_rope_elems <= 0)
+        return LTX3DROPE_E_INVALID;
+    const int64_t n = dim / num_rope_elems;
+    if (n > (int64_t(1) << 24)) return LTX3DROPE_E_INVALID;
+    if (count != nullptr) *count = n;
+    if (n == 0) return LTX3DROPE_OK;
+    if (out == nullptr) return LTX3DROPE_E_INVALID;
+    hipPointerAttribute_t a;
+    std::memset(&a, 0, sizeof(a));
+    if (hipPointerGetAttributes(&a, out) != hipSuccess || a.type != hipMemoryTypeDevice) {
+        (void)hipGetLastError();
+        stats().rejected.fetch_add(1);
+        return LTX3DROPE_E_UNSUPPORTED;
+    }
+    if (check_device_ptr(out, static_cast<size_t>(n) * sizeof(float), a.device) != LTX3DROPE_REASON_OK) {
+        stats().rejected.fetch_add(1);
+        return LTX3DROPE_E_UNSUPPORTED;
+    }
+    DeviceGuard guard(a.device);
+    if (launch_dit_freqs(out, static_cast<uint32_t>(n), theta, double_precision != 0, static_cast<hipStream_t>(stream)) !=
+            hipSuccess ||
+        hipGetLastError() != hipSuccess)
+        return LTX3DROPE_E_HIP;
+    stats().fast.fetch_add(1);
+    return LTX3DROPE_OK;
+}
+
 int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads,
                          int64_t head_dim, int64_t dim_t, int64_t dim_h, int64_t dim_w) {
     return gate_get(GateKey{device, dtype, B, T, H, W, heads, head_dim, dim_t, dim_h, dim_w});

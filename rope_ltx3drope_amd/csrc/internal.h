@@ -26,7 +26,8 @@ struct ltx3drope_tables {
 namespace ltx3drope {
 
 // Everything a kernel needs to know about one apply_qk call.  All sizes fit in
-// 32 bits because the precheck caps every tensor below 2^31 elements.
+// 32 bits because the precheck caps every tensor below 2^32 elements (pairs
+// below 2^31, 16-byte vectors below 2^30).
 struct Problem {
     void* q_out;
     void* k_out;
@@ -82,6 +83,9 @@ struct PatchProblem {
 };
 bool patch_fast_supported(const PatchProblem& p);
 hipError_t launch_patch(const PatchProblem& p, bool inverse, hipStream_t stream, int cu_count);
+
+// The LTX DiT RoPE frequency grid, n values into device memory (dit_freqs.hip).
+hipError_t launch_dit_freqs(float* out, uint32_t n, double theta, bool double_precision, hipStream_t stream);
 
 // Tables and cache (tables.cpp).
 int tables_build(int device, int64_t T, int64_t H, int64_t W, int64_t dim_t, int64_t dim_h, int64_t dim_w,

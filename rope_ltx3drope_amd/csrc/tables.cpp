@@ -245,47 +245,3 @@ void cache_counters_reset() {
 }
 
 }  // namespace ltx3drope
-
-// LTX DiT RoPE frequency grid (sglang PR #24660 page, "Key source snippets").
-extern "C" int ltx3drope_dit_freq_grid(double theta, int64_t dim, int64_t num_rope_elems, int double_precision,
-                                       float* out, int out_on_device, void* stream, int64_t* count) {
-    if (!std::isfinite(theta) || theta <= 0.0 || dim < 0 || num_rope_elems <= 0) return LTX3DROPE_E_INVALID;
-    const int64_t n = dim / num_rope_elems;
-    if (n > (int64_t(1) << 24)) return LTX3DROPE_E_INVALID;
-    if (count != nullptr) *count = n;
-    if (n == 0) return LTX3DROPE_OK;
-    if (out == nullptr) return LTX3DROPE_E_INVALID;
-    std::vector<float> host;
-    try {
-        host.resize(static_cast<size_t>(n));
-    } catch (...) {
-        return LTX3DROPE_E_NOMEM;
-    }
-    const double pi = M_PI;
-    for (int64_t i = 0; i < n; ++i) {
-        const double xd = n > 1 ? static_cast<double>(i) / static_cast<double>(n - 1) : 0.0;
-        if (double_precision) {
-            const double p = std::pow(theta, xd);
-            const double prod = p * pi;
-            host[static_cast<size_t>(i)] = static_cast<float>(prod / 2.0);
-        } else {
-            const float xf = static_cast<float>(xd);
-            const float th = static_cast<float>(theta);
-            const float p = static_cast<float>(std::pow(static_cast<double>(th), static_cast<double>(xf)));
-            const float prod = p * static_cast<float>(pi);
-            host[static_cast<size_t>(i)] = prod / 2.0f;
-        }
-    }
-    const size_t bytes = static_cast<size_t>(n) * sizeof(float);
-    if (!out_on_device) {
-        std::memcpy(out, host.data(), bytes);
-        return LTX3DROPE_OK;
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (hipMemcpyAsync(out, host.data(), bytes, hipMemcpyHostToDevice, s) != hipSuccess ||
-        hipStreamSynchronize(s) != hipSuccess) {
-        (void)hipGetLastError();
-        return LTX3DROPE_E_HIP;
-    }
-    return LTX3DROPE_OK;
-}

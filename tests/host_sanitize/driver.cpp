@@ -98,14 +98,16 @@ void worker(int id, int iters, std::atomic<int>* failures) {
             CHECK(s.cache_live >= 0 && s.cache_live <= 16 && s.tables_alive >= 0);
         }
         if (rng() % 17 == 0) {
-            const int64_t dim = static_cast<int64_t>(rng() % 5000);
+            // the DiT grid's argument checks: an empty grid (dim < num_rope_elems) and refused
+            // arguments return before any HIP call
             const int64_t ne = 1 + static_cast<int64_t>(rng() % 8);
-            std::vector<float> grid(static_cast<size_t>(dim / ne) + 1, -1.0f);
+            const int64_t dim = static_cast<int64_t>(rng() % static_cast<uint64_t>(ne));
             int64_t n = -1;
-            CHECK(ltx3drope_dit_freq_grid(10000.0, dim, ne, static_cast<int>(rng() % 2), grid.data(), 0, nullptr, &n) ==
+            CHECK(ltx3drope_dit_freq_grid(10000.0, dim, ne, static_cast<int>(rng() % 2), nullptr, nullptr, &n) ==
                   LTX3DROPE_OK);
-            CHECK(n == dim / ne);
-            if (n > 0) CHECK(std::fabs(grid[0] - 1.5707964f) < 1e-6f);
+            CHECK(n == 0);
+            CHECK(ltx3drope_dit_freq_grid(-1.0, 64, ne, 1, nullptr, nullptr, &n) == LTX3DROPE_E_INVALID);
+            CHECK(ltx3drope_dit_freq_grid(10000.0, 64, 2, 0, nullptr, nullptr, &n) == LTX3DROPE_E_INVALID);
         }
     }
     for (ltx3drope_tables_t t : held) CHECK(ltx3drope_tables_release(t) == LTX3DROPE_OK);

@@ -14,6 +14,7 @@
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -45,6 +46,24 @@ def torch_page_expression(theta, dim, ne, double):
 # ---------------------------------------------------------------------------
 # pins (each a plain function, so the planted-mistake test can run them)
 # ---------------------------------------------------------------------------
+
+def pin_round_to_ieee_casts():
+    """The exact rounding helper against numpy's IEEE float64 -> float32 conversion on doubles (a
+    correctly rounded cast): random values, exact float32 midpoints, and the overflow boundary."""
+    rng = np.random.default_rng(5)
+    vals = list(rng.standard_normal(2000) * 10.0 ** rng.integers(-30, 30, 2000))
+    f32 = rng.standard_normal(500).astype(np.float32)
+    vals += [float(np.float64(v) + np.float64(np.spacing(v)) / 2) for v in f32]  # exact midpoints
+    flt_max = float(np.finfo(np.float32).max)
+    vals += [flt_max, 2.0 ** 128 - 2.0 ** 103, 2.0 ** 128 - 2.0 ** 102, -(2.0 ** 128 - 2.0 ** 103), 2.0 ** 128]
+    with np.errstate(over="ignore"):
+        for v in vals:
+            got = df.round_to(Fraction(v), False)
+            want = np.float32(v)
+            assert got.view(np.uint32) == want.view(np.uint32), (v, got, want)
+    assert df.round_to(Fraction(2) ** 1024, True) == np.inf
+    assert df.round_to(Fraction(1, 3), True) == np.float64(1.0) / np.float64(3.0)
+
 
 def pin_linspace_torch():
     for double in (True, False):
@@ -122,6 +141,10 @@ def pin_grid_closed_forms():
 # tests
 # ---------------------------------------------------------------------------
 
+def test_round_to_matches_ieee_casts():
+    pin_round_to_ieee_casts()
+
+
 def test_linspace_equals_torch_bitwise():
     pin_linspace_torch()
 
@@ -195,7 +218,7 @@ MISTAKES = [("linspace", _linspace_correctly_rounded_ratio), ("linspace", _linsp
 def test_planted_mistake_is_caught(monkeypatch, name, impl):
     monkeypatch.setitem(df.__dict__, "_orig_" + name, getattr(df, name))
     monkeypatch.setattr(df, name, impl)
-    pins = [pin_linspace_torch, pin_pow_closed_forms, pin_pow_libm, pin_grid_closed_forms,
+    pins = [pin_round_to_ieee_casts, pin_linspace_torch, pin_pow_closed_forms, pin_pow_libm, pin_grid_closed_forms,
             lambda: pin_grid_torch(10000.0, 4096, 6, True), lambda: pin_grid_torch(500.0, 96, 3, False)]
     caught = 0
     for pin in pins:

@@ -649,16 +649,6 @@ def test_inplace_matches_out_of_place_and_respects_the_gate(dtype):
         assert_bitexact(to_host(dk, dtype), want_k, dtype, "k in place (fast)")
 
 
-def test_dit_freq_grid_on_device_equals_host():
-    import oracle.dit_freqs as df
-
-    for double in (True, False):
-        d = rla.dit_freq_grid(10000.0, 4096, 6, double, device=DEV)
-        torch.cuda.synchronize()
-        np.testing.assert_array_equal(d.cpu().numpy().view(np.uint32),
-                                      df.freq_grid(10000.0, 4096, 6, double).view(np.uint32))
-
-
 def test_largest_supported_tensor():
     """31 heads x [1, 16, 64, 1024] x head_dim 128 = 4,160,749,568 elements per tensor (7.75 GiB of
     bf16), just under the 2^32 limit: the gate's full-size verification, fast == plain over the

@@ -505,10 +505,13 @@ def test_neox_precheck_rules():
 
 def test_dit_freq_grid_rejects_bad_arguments():
     n = ctypes.c_int64(-1)
-    for args in ((0.0, 64, 2), (-1.0, 64, 2), (float("inf"), 64, 2), (1e4, -1, 2), (1e4, 64, 0)):
-        assert L.ltx3drope_dit_freq_grid(*args, 1, None, 0, None, ctypes.byref(n)) == _lib.E_INVALID
-    assert L.ltx3drope_dit_freq_grid(1e4, 64, 2, 1, None, 0, None, ctypes.byref(n)) == _lib.E_INVALID  # NULL out
-    assert L.ltx3drope_dit_freq_grid(1e4, 1, 2, 1, None, 0, None, ctypes.byref(n)) == _lib.OK and n.value == 0
+    for args in ((0.0, 64, 2), (-1.0, 64, 2), (float("inf"), 64, 2), (float("nan"), 64, 2), (1e-39, 64, 2),
+                 (3.5e38, 64, 2), (1e4, -1, 2), (1e4, 64, 0), (1e4, (1 << 24) + 1, 1)):
+        assert L.ltx3drope_dit_freq_grid(*args, 1, None, None, ctypes.byref(n)) == _lib.E_INVALID
+    assert L.ltx3drope_dit_freq_grid(1e4, 64, 2, 1, None, None, ctypes.byref(n)) == _lib.E_INVALID  # NULL out
+    assert L.ltx3drope_dit_freq_grid(1e4, 1, 2, 1, None, None, ctypes.byref(n)) == _lib.OK and n.value == 0
+    host = (ctypes.c_float * 32)()
+    assert L.ltx3drope_dit_freq_grid(1e4, 64, 2, 1, host, None, ctypes.byref(n)) in (_lib.E_UNSUPPORTED, _lib.E_HIP)
 
 
 def test_binding_refuses_host_tensors_and_bad_patch_sizes_before_any_call():
