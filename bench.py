@@ -16,10 +16,11 @@ duration: the time between two HIP events recorded on the kernel's stream before
 the first and after the last of the K timed launches, divided by K (the launches
 run back to back; no marker sits between two kernels).  The CPU leg (the
 cpu_leg_* functions, the only code here that runs the oracle, which is test
-infrastructure) computes the oracle's result on a bounded sample of the same
-workload: the GPU's timed outputs are compared with it element by element
-(parity), and the oracle's time on the host over a longer sample, scaled to the
-same unit, is cpu_baseline (skipped with --no-cpu-baseline).
+infrastructure) computes the oracle's result for the whole workload on a pool of
+threads and compares every element of the GPU's timed outputs with it (parity;
+in place: sampled tokens), and times the oracle on one core over a bounded
+sample of the same workload, scaled to the same unit: cpu_baseline (skipped with
+--no-cpu-baseline; the pool pass is reported under all_cores).
 
 --op neox | patchify | unpatchify time the secondary kernels the same way
 (200 warm-up and 200 timed launches of about 0.13 ms each by default), with
@@ -108,8 +109,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--cpu-threads", type=int, default=None,
-                    help="rope3d: threads of the additional all-cores oracle run (default: the usable cores, "
-                         "at most 16; 0 or 1 skips it)")
+                    help="rope3d: threads of the oracle's pass over the whole workload that checks every output "
+                         "element (default: the usable cores, at most 16)")
     ap.add_argument("--op", choices=("rope3d", "neox", "patchify", "unpatchify", "dit_freqs"), default="rope3d",
                     help="rope3d: the fused 3D RoPE (default); neox: the rotate-half RoPE with a gathered cache; "
                          "patchify / unpatchify: the stage-5 space-to-depth and its inverse")
@@ -420,10 +421,10 @@ def main_cycle(args):
     achieved = alg_pass * args.steps / gpu_s / 1e9
     value = alg_pass / (wall / args.steps) / 1e9
 
-    parity = {"sampled_tokens": 0, "mismatching_elements": 0, "tolerance_ulp": 0}
-    for gi, (q_np, k_np) in zip(grids, host):  # every grid's last outputs
-        pg, _ = cpu_leg_rope3d(w, gi, q_np, k_np, *last[gi], 0, args, count=128, seed=4321 + gi, time_it=False)
-        parity["sampled_tokens"] += pg["sampled_tokens"]
+    parity = {"compared_elements": 0, "mismatching_elements": 0, "tolerance_ulp": 0}
+    for gi, (q_np, k_np) in zip(grids, host):  # every element of every grid's last outputs
+        pg, _ = cpu_leg_rope3d(w, gi, q_np, k_np, *last[gi], 0, args, time_it=False)
+        parity["compared_elements"] += pg["compared_elements"]
         parity["mismatching_elements"] += pg["mismatching_elements"]
     copy_gbs = copy_ceiling([inputs[grids[0]]], stream)
     line = {
@@ -746,10 +747,12 @@ def patch_workload_name(op: str, shape, p: int, elem_bytes: int) -> str:
 # the oracle on the host cores over a longer sample (the line's "cpu_baseline").
 # ---------------------------------------------------------------------------
 
-def cpu_leg_rope3d(w, gi, q_np, k_np, qo, ko, rotations, args, count=256, seed=1234, time_it=True):
-    """3D RoPE: the oracle on `count` sampled tokens of grid `gi` against the GPU outputs qo, ko
-    (rotations > 0: in-place mode, the oracle applied that many times to the input rows), then
-    the timed oracle on whole (batch, frame) slabs.  Returns (parity, cpu_baseline or None)."""
+def cpu_leg_rope3d(w, gi, q_np, k_np, qo, ko, rotations, args, time_it=True):
+    """3D RoPE.  Parity: every element of the GPU outputs qo, ko against the oracle, computed over
+    blocks of rows of each (batch, frame) by a pool of threads (that pass, timed, is also the
+    all-cores CPU figure); in place (rotations > 0) the oracle applied that many times to 256
+    sampled tokens instead.  Then, unless --no-cpu-baseline, the oracle timed on one core over whole
+    (batch, frame) slabs.  Returns (parity, cpu_baseline or None)."""
     import numpy as np
     import torch
 
@@ -757,26 +760,88 @@ def cpu_leg_rope3d(w, gi, q_np, k_np, qo, ko, rotations, args, count=256, seed=1
     import workloads
 
     B, T, H, W, heads, D = w.shape(gi)
-    ids = workloads.sample_tokens(B * T * H * W, count, seed=seed)
-    idx = torch.from_numpy(ids).to(qo.device)
-    mism = 0
-    for x_np, out in ((q_np, qo), (k_np, ko)):
-        if rotations:
-            tabs = oracle.grid_tables(T, H, W, w.split, w.base)
-            coords = oracle.token_coords(ids, T, H, W)
+    if rotations:
+        ids = workloads.sample_tokens(B * T * H * W, 256, seed=1234)
+        idx = torch.from_numpy(ids).to(qo.device)
+        tabs = oracle.grid_tables(T, H, W, w.split, w.base)
+        coords = oracle.token_coords(ids, T, H, W)
+        mism = 0
+        for x_np, out in ((q_np, qo), (k_np, ko)):
             want = x_np.reshape(B * T * H * W, heads, D)[ids]
             for _ in range(rotations):
                 want = oracle.apply_rope_tokens(want, w.dtype, coords, tabs, w.split)
-        else:
-            want = oracle.rope3d_sampled(x_np, w.dtype, w.split, ids, w.base)
-        got = out.view(B * T * H * W, heads, D)[idx].cpu()
-        got = got.view(torch.int16).numpy().view(np.uint16) if w.itemsize == 2 else got.numpy()
-        mism += int((got.view(want.dtype) != want).sum())
-    parity = {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0}
+            got = _host_bits(out.view(B * T * H * W, heads, D)[idx], w.itemsize)
+            mism += int((got.view(want.dtype) != want).sum())
+        parity = {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0}
+        all_cores = None
+    else:
+        threads = max(1, args.cpu_threads)
+        t0 = time.perf_counter()
+        mism, first = 0, None
+        for x_np, out in ((q_np, qo), (k_np, ko)):
+            m, f = cpu_leg_compare_all(x_np, _host_bits(out, w.itemsize), w.dtype, w.split, w.base, threads)
+            mism += m
+            first = first or f
+        dt = time.perf_counter() - t0
+        parity = {"compared_elements": int(2 * q_np.size), "mismatching_elements": mism, "tolerance_ulp": 0}
+        if first:
+            parity["first_mismatch"] = first
+        n = 2 * q_np.size
+        all_cores = {"value": round(n * 2 * w.itemsize / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+                     "gelem_per_s": round(n / dt / 1e9, 5), "seconds": round(dt, 2),
+                     "sample": f"the whole workload once (Q and K, {n} elements), blocks of rows of each (batch, "
+                               f"frame) on {threads} threads, compared with the GPU outputs (includes the "
+                               "comparison)"}
     cpu = None
     if time_it and not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, gi, q_np, k_np, args.cpu_seconds, args.cpu_threads)
+        cpu = cpu_baseline(w, gi, q_np, k_np, args.cpu_seconds)
+        if all_cores is not None:
+            cpu["all_cores"] = all_cores
     return parity, cpu
+
+
+def _host_bits(t, itemsize: int):
+    """A device tensor's contents on the host as raw uint16 (bf16) or float32 values."""
+    import numpy as np
+    import torch
+
+    h = t.detach().cpu()
+    return h.view(torch.int16).numpy().view(np.uint16) if itemsize == 2 else h.numpy()
+
+
+def cpu_leg_compare_all(x_np, got_np, dtype, split, base, threads: int):
+    """(mismatching elements, first mismatch or None): the oracle applied to every block of up to
+    8 M elements (rows of one (batch, frame), a shard of the whole grid with the whole grid's
+    tables) from a pool of threads, each block compared bit for bit with got_np."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    B, T, H, W, heads, D = x_np.shape
+    tables = oracle.grid_tables(T, H, W, split, base)
+    rows = max(1, min(H, (1 << 23) // (W * heads * D)))
+    view = (lambda a: a.view(np.uint32)) if got_np.dtype == np.float32 else (lambda a: a)
+
+    def block(job):
+        b, t, h0 = job
+        h1 = min(H, h0 + rows)
+        want = oracle.rope3d(np.ascontiguousarray(x_np[b:b + 1, t:t + 1, h0:h1]), dtype, split, base,
+                             tables=tables, offsets=(t, h0, 0), grid=(T, H, W))
+        got = got_np[b:b + 1, t:t + 1, h0:h1]
+        neq = view(got) != view(want)
+        n = int(neq.sum())
+        if not n:
+            return 0, None
+        i = tuple(int(v) for v in np.argwhere(neq)[0])
+        return n, {"index": [b, t, h0 + i[2]] + list(i[3:]), "got": hex(int(view(got)[i])),
+                   "want": hex(int(view(want)[i]))}
+
+    jobs = [(b, t, h0) for b in range(B) for t in range(T) for h0 in range(0, H, rows)]
+    with ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(block, jobs))
+    return sum(n for n, _ in res), next((f for n, f in res if n), None)
 
 
 def cpu_leg_neox(w, q_np, k_np, pos_np, cache_np, qo, ko, args):
@@ -883,64 +948,37 @@ def neox_cpu_baseline(w, q_np, k_np, pos_np, cache_np, target_s):
                       f"{chunk}-token chunks, Q and K; numpy, one thread pinned to one core; CPU: {_cpu_model()}"}
 
 
-def cpu_baseline(w, gi, q_np, k_np, target_s, threads=0):
-    """The oracle, untuned, on whole (batch, frame) slabs of the same inputs (Q and K), single thread,
-    until about target_s seconds of CPU work are done.  With threads > 1, also the same oracle on
-    every slab from a pool of that many threads (numpy releases the interpreter lock inside its
-    array operations), whole passes over the workload for about target_s / 2 seconds, under
-    "all_cores"."""
+def cpu_baseline(w, gi, q_np, k_np, target_s):
+    """The oracle, untuned, on whole (batch, frame) slabs of the same inputs (Q and K), single thread
+    pinned to one core, until about target_s seconds of CPU work are done (or every slab is)."""
     import numpy as np
 
     import oracle
 
     B, T, H, W, heads, D = w.shape(gi)
+    pin_one_core()
     t0 = time.perf_counter()
     tabs = oracle.grid_tables(T, H, W, w.split, w.base)
     t_tab = time.perf_counter() - t0
     per_slab = 2 * H * W * heads * D
-
-    def slab(i):
-        b, t = divmod(i, T)
-        for x in (q_np, k_np):
-            oracle.rope3d(np.ascontiguousarray(x[b:b + 1, t:t + 1]), w.dtype, w.split, w.base,
-                          tables=_slice_tables(tabs, t))
-        return per_slab
-
-    all_cores = None
-    if threads > 1:
-        from concurrent.futures import ThreadPoolExecutor
-
-        done, passes = 0, 0
-        t0 = time.perf_counter()
-        with ThreadPoolExecutor(threads) as ex:
-            while True:
-                done += sum(ex.map(slab, range(B * T)))
-                passes += 1
-                if time.perf_counter() - t0 >= target_s / 2:
-                    break
-        dt = time.perf_counter() - t0
-        all_cores = {"value": round(done / dt * 2 * w.itemsize / 1e9, 4), "unit": "GB/s", "cores": threads,
-                     "gelem_per_s": round(done / dt / 1e9, 5), "seconds": round(dt, 2),
-                     "sample": f"{passes} whole pass(es) over the {B * T} (batch, frame) slabs, Q and K, tables "
-                               f"prebuilt; {threads} threads"}
-    pin_one_core()
     done = 0
     slabs = 0
     t0 = time.perf_counter()
     while slabs < B * T:
-        done += slab(slabs)
+        b, t = divmod(slabs, T)
+        for x in (q_np, k_np):
+            oracle.rope3d(np.ascontiguousarray(x[b:b + 1, t:t + 1]), w.dtype, w.split, w.base,
+                          tables=_slice_tables(tabs, t))
+        done += per_slab
         slabs += 1
         if time.perf_counter() - t0 >= target_s:
             break
     dt = time.perf_counter() - t0 + t_tab
     eps = done / dt
-    out = {"value": round(eps * 2 * w.itemsize / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "gelem_per_s": round(eps / 1e9, 5), "seconds": round(dt, 2),
-           "sample": f"{slabs} of {B * T} (batch, frame) slabs, Q and K ({done} elements), plus the grid's "
-                     f"table build; numpy, one thread pinned to one core; CPU: {_cpu_model()}"}
-    if all_cores is not None:
-        out["all_cores"] = all_cores
-    return out
+    return {"value": round(eps * 2 * w.itemsize / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "gelem_per_s": round(eps / 1e9, 5), "seconds": round(dt, 2),
+            "sample": f"{slabs} of {B * T} (batch, frame) slabs, Q and K ({done} elements), plus the grid's "
+                      f"table build; numpy, one thread pinned to one core; CPU: {_cpu_model()}"}
 
 
 def _slice_tables(tabs, t):

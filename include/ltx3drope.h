@@ -188,9 +188,13 @@ int ltx3drope_can_use(const void* q_out, const void* k_out, const void* q, const
  * call verified; equal -> the fast path is trusted, unequal -> permanent
  * fallback to the plain path for that configuration).  The gate's
  * configuration key is (device, dtype, B, T, H, W, heads, head_dim, dim_t,
- * dim_h, dim_w).  The first verification on a device allocates that device's
- * 256-byte counter, kept until the process ends: E_NOMEM if the device is out
- * of memory, E_HIP for any other failed HIP call or launch.
+ * dim_h, dim_w).  The comparison is of raw bits: both kernels write a NaN
+ * result as the canonical quiet NaN (0x7FC00000 fp32, 0x7FC0 bf16).  On a
+ * stream under graph capture an unverified configuration runs the plain
+ * kernel and stays unverified (the check cannot wait for its count there).
+ * The first verification on a device allocates that device's 256-byte
+ * counter, kept until the process ends: E_NOMEM if the device is out of
+ * memory, E_HIP for any other failed HIP call or launch.
  */
 int ltx3drope_apply_qk(void* q_out, void* k_out, const void* q, const void* k, int dtype,
                        int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,

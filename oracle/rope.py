@@ -103,8 +103,20 @@ def to_f32(x: np.ndarray, dtype: str) -> np.ndarray:
     return bf16_bits_to_f32(x) if dtype == BF16 else np.asarray(x, dtype=np.float32)
 
 
+def f32_canonical_nan(y: np.ndarray) -> np.ndarray:
+    """fp32 values with every NaN replaced by the canonical quiet NaN 0x7FC00000 (the pages are
+    silent on NaN payloads; one fixed pattern makes equal inputs give byte-identical outputs)."""
+    y = np.asarray(y, dtype=np.float32)
+    nan = np.isnan(y)
+    if not nan.any():
+        return y
+    out = y.copy()
+    out.view(np.uint32)[nan] = np.uint32(0x7FC00000)
+    return out
+
+
 def from_f32(y: np.ndarray, dtype: str) -> np.ndarray:
-    return f32_to_bf16_bits(y) if dtype == BF16 else np.asarray(y, dtype=np.float32)
+    return f32_to_bf16_bits(y) if dtype == BF16 else f32_canonical_nan(y)
 
 
 # ---------------------------------------------------------------------------

@@ -366,6 +366,14 @@ int apply_impl(void* q_out, void* k_out, const void* q, const void* k, int dtype
                           device);
     }
     if (state == LTX3DROPE_GATE_TRUSTED && gate_mode == 1) return run_kernel(Kernel::Fast, p, stream, device);
+    // The verification waits for its count on the host, which a stream under graph capture cannot
+    // do: such a call runs the plain kernel and leaves the configuration unverified.
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &capture) != hipSuccess) {
+        (void)hipGetLastError();
+        capture = hipStreamCaptureStatusNone;
+    }
+    if (capture != hipStreamCaptureStatusNone) return run_kernel(Kernel::Plain, p, stream, device);
 
     bool equal = false;
     const int st = verify_fast(p, stream, device, &equal);

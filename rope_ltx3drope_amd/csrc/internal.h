@@ -53,7 +53,7 @@ bool fast_supported(const Problem& p);
 hipError_t launch_fast(const Problem& p, hipStream_t stream, int device);
 hipError_t launch_plain(const Problem& p, hipStream_t stream, int device);
 // Recompute with the plain kernel and count the pairs whose result differs
-// from what q_out/k_out already hold (bit patterns; two NaNs count as equal).
+// from what q_out/k_out already hold (raw bit patterns).
 hipError_t launch_verify(const Problem& p, unsigned* mismatches, hipStream_t stream, int device);
 hipError_t launch_zero_u32(unsigned* ptr, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream, int device);

@@ -6,7 +6,9 @@
 // followed by one rounded difference and one rounded sum; no fused
 // multiply-add.  This file is compiled with -ffp-contract=off and the pragma
 // below, and every product/sum goes through __fmul_rn/__fsub_rn/__fadd_rn.
-// The result is cast back to the tensor dtype with round-to-nearest-even.
+// The result is cast back to the tensor dtype with round-to-nearest-even.  A
+// NaN result is written as the canonical quiet NaN (0x7FC00000 in fp32, 0x7FC0
+// in bf16) by both kernels, so equal inputs give byte-identical outputs.
 //
 // Index mapping (same snippet): pair j of a head uses the t table at column j
 // for j < dim_t/2, the h table at column j - dim_t/2 for j < (dim_t+dim_h)/2,
@@ -14,11 +16,15 @@
 // coordinate, with token n = (t*H + h)*W + w in each batch element.
 //
 // Two kernels compute it:
-//  * rope_plain: one pair per thread, every index derived from the flat pair
-//    index, scalar loads and stores, integer round-to-nearest-even.  It is the
-//    reference path of the bit-exact gate and the fallback for shapes the fast
-//    kernel does not cover.  With VERIFY it recomputes the result and counts
-//    pairs that differ from what the outputs already hold.
+//  * rope_plain: one thread per (token, head) row of Q or of K, written from
+//    the eager definition: the thread finds its token's (t, h, w) from the
+//    row's place in the contiguous [B, T, H, W, heads, head_dim] layout, then
+//    walks the time, height and width chunks of the row in turn, rotating each
+//    chunk's pairs with the table row of that axis's coordinate; scalar loads
+//    and stores, integer round-to-nearest-even.  It is the reference path of
+//    the bit-exact gate and the fallback for shapes the fast kernel does not
+//    cover.  With VERIFY it recomputes the result and counts pairs whose bits
+//    differ from what the outputs already hold.
 //  * rope_fast: a one-shot grid in which each thread owns one 16-byte vector
 //    (8 bf16 or 4 fp32 values, i.e. 4 or 2 pairs): the first half of the grid
 //    covers Q, the second half K.  When a token's heads*head_dim row is a whole
@@ -53,13 +59,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kFastBlock = 64;             // one wavefront per workgroup
 constexpr int kPlainBlock = 256;
 
+// The pair (e, o) turned by the angle whose cosine and sine are (c, s): four
+// products, each rounded to fp32, then one rounded difference (even result)
+// and one rounded sum (odd result); nothing is fused.
 __device__ __forceinline__ void rotate(float e, float o, float c, float s, float& ye, float& yo) {
-    const float even_cos = __fmul_rn(e, c);
-    const float odd_sin = __fmul_rn(o, s);
-    const float even_sin = __fmul_rn(e, s);
-    const float odd_cos = __fmul_rn(o, c);
-    ye = __fsub_rn(even_cos, odd_sin);
-    yo = __fadd_rn(even_sin, odd_cos);
+    const float ec = __fmul_rn(e, c), os_ = __fmul_rn(o, s);
+    const float es = __fmul_rn(e, s), oc = __fmul_rn(o, c);
+    ye = __fsub_rn(ec, os_);
+    yo = __fadd_rn(es, oc);
 }
 
 // bf16 <-> fp32.  A 32-bit word holds one pair: the even element in the low half.
@@ -73,95 +80,81 @@ __device__ __forceinline__ uint32_t bf16_rne_int(float y) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Hardware conversion of two floats to a packed bf16 pair (round to nearest even).
+// fp32 bits with any NaN replaced by the canonical quiet NaN.
+__device__ __forceinline__ uint32_t f32_canon(float y) { return y != y ? 0x7fc00000u : __float_as_uint(y); }
+
+// Hardware conversion of two floats to a packed bf16 pair (round to nearest
+// even), then any NaN half replaced by the canonical quiet NaN 0x7FC0.
 __device__ __forceinline__ uint32_t bf16_pack_hw(float lo, float hi) {
     const f32x2 v = {lo, hi};
     const bf16x2 r = __builtin_convertvector(v, bf16x2);
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ bool same_bits_or_both_nan_f32(uint32_t a, uint32_t b) {
-    return a == b || (((a & 0x7fffffffu) > 0x7f800000u) && ((b & 0x7fffffffu) > 0x7f800000u));
-}
-
-__device__ __forceinline__ bool same_bits_or_both_nan_bf16(uint32_t a, uint32_t b) {
-    return a == b || (((a & 0x7fffu) > 0x7f80u) && ((b & 0x7fffu) > 0x7f80u));
+    uint32_t w = __builtin_bit_cast(uint32_t, r);
+    if (lo != lo) w = (w & 0xffff0000u) | 0x7fc0u;
+    if (hi != hi) w = (w & 0x0000ffffu) | 0x7fc00000u;
+    return w;
 }
 
 // ---------------------------------------------------------------------------
-// plain kernel: one pair per thread
+// plain kernel: one (token, head) row per thread
 // ---------------------------------------------------------------------------
 
 struct PlainArgs {
-    const void* q;
-    const void* k;
-    void* q_out;
-    void* k_out;
-    const float2* tab;
+    const void* src[2];  // Q, K
+    void* dst[2];        // Q_out, K_out
+    const float2* tab;   // packed (cos, sin) pairs: the t section, then h, then w
     unsigned* mismatches;
-    uint32_t pairs;  // pairs per tensor
-    uint32_t pph;    // pairs per head = D/2
-    uint32_t heads, N, HW, W;
-    uint32_t PT, PH;
-    uint32_t offH, offW;  // first pair of the h and w table sections
-    uint32_t PW;
-    uint32_t t_off, h_off, w_off;  // global coordinate of the tensor's first frame / row / column
+    uint32_t rows;              // (token, head) rows per tensor, B*T*H*W*heads; the grid covers both tensors
+    uint32_t heads, half_dim;   // heads per token, pairs per head row (head_dim / 2)
+    uint32_t T, H, W;           // the tensor's grid
+    uint32_t origin[3];         // coordinate of the tensor's first frame / row / column in the tables' grid
+    uint32_t width[3];          // pairs of the t, h and w chunks of a head row
+    uint32_t section[3];        // first pair of the t, h and w sections of the packed tables
 };
 
 template <bool BF16, bool VERIFY>
 __global__ void __launch_bounds__(kPlainBlock) rope_plain(PlainArgs a) {
-    const uint32_t stride = gridDim.x * blockDim.x;
     uint32_t bad = 0;
-    for (uint32_t p = blockIdx.x * blockDim.x + threadIdx.x; p < a.pairs; p += stride) {
-        const uint32_t j = p % a.pph;
-        const uint32_t row = p / a.pph;      // (token, head)
-        const uint32_t token = row / a.heads;
-        const uint32_t n = token % a.N;      // position inside the batch element
-        const uint32_t t = n / a.HW;
-        const uint32_t rem = n - t * a.HW;
-        const uint32_t h = rem / a.W;
-        const uint32_t w = rem - h * a.W;
-        uint32_t idx;
-        if (j < a.PT) {
-            idx = (t + a.t_off) * a.PT + j;
-        } else if (j < a.PT + a.PH) {
-            idx = a.offH + (h + a.h_off) * a.PH + (j - a.PT);
-        } else {
-            idx = a.offW + (w + a.w_off) * a.PW + (j - a.PT - a.PH);
-        }
-        const float2 cs = a.tab[idx];
-        if constexpr (BF16) {
-            const uint32_t* src[2] = {static_cast<const uint32_t*>(a.q), static_cast<const uint32_t*>(a.k)};
-            uint32_t* dst[2] = {static_cast<uint32_t*>(a.q_out), static_cast<uint32_t*>(a.k_out)};
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const uint32_t in = src[x][p];
+    // 2 * rows < 2^32 (a tensor holds fewer than 2^32 elements, a row at least 2); the index is
+    // 64-bit so that adding the grid stride cannot wrap
+    const uint64_t items = 2ull * a.rows;
+    for (uint64_t item = blockIdx.x * kPlainBlock + threadIdx.x; item < items; item += gridDim.x * kPlainBlock) {
+        const uint32_t x = item < a.rows ? 0 : 1;  // 0: Q, 1: K
+        const uint32_t row = static_cast<uint32_t>(item - x * uint64_t(a.rows));
+        // row = ((((b*T + t)*H + h)*W + w)*heads + head: peel the layout from the innermost axis out
+        uint32_t rest = row / a.heads;
+        uint32_t coord[3];
+        coord[2] = rest % a.W;
+        rest /= a.W;
+        coord[1] = rest % a.H;
+        rest /= a.H;
+        coord[0] = rest % a.T;
+        uint32_t pair = row * a.half_dim;  // first (even, odd) pair of the row; < 2^31
+        for (int axis = 0; axis < 3; ++axis) {
+            const float2* cs_row = a.tab + a.section[axis] + (coord[axis] + a.origin[axis]) * a.width[axis];
+            for (uint32_t i = 0; i < a.width[axis]; ++i, ++pair) {
+                const float2 cs = cs_row[i];
                 float ye, yo;
-                rotate(bf16_lo(in), bf16_hi(in), cs.x, cs.y, ye, yo);
-                const uint32_t lo = bf16_rne_int(ye), hi = bf16_rne_int(yo);
-                if constexpr (VERIFY) {
-                    const uint32_t have = dst[x][p];
-                    if (!same_bits_or_both_nan_bf16(have & 0xffffu, lo) || !same_bits_or_both_nan_bf16(have >> 16, hi))
-                        ++bad;
+                if constexpr (BF16) {
+                    const uint32_t in = static_cast<const uint32_t*>(a.src[x])[pair];
+                    rotate(bf16_lo(in), bf16_hi(in), cs.x, cs.y, ye, yo);
+                    const uint32_t out = bf16_rne_int(ye) | (bf16_rne_int(yo) << 16);
+                    uint32_t* dst = static_cast<uint32_t*>(a.dst[x]) + pair;
+                    if constexpr (VERIFY) {
+                        bad += *dst != out ? 1u : 0u;
+                    } else {
+                        *dst = out;
+                    }
                 } else {
-                    dst[x][p] = lo | (hi << 16);
-                }
-            }
-        } else {
-            const float2* src[2] = {static_cast<const float2*>(a.q), static_cast<const float2*>(a.k)};
-            float2* dst[2] = {static_cast<float2*>(a.q_out), static_cast<float2*>(a.k_out)};
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const float2 in = src[x][p];
-                float ye, yo;
-                rotate(in.x, in.y, cs.x, cs.y, ye, yo);
-                if constexpr (VERIFY) {
-                    const float2 have = dst[x][p];
-                    if (!same_bits_or_both_nan_f32(__float_as_uint(have.x), __float_as_uint(ye)) ||
-                        !same_bits_or_both_nan_f32(__float_as_uint(have.y), __float_as_uint(yo)))
-                        ++bad;
-                } else {
-                    dst[x][p] = make_float2(ye, yo);
+                    const float2 in = static_cast<const float2*>(a.src[x])[pair];
+                    rotate(in.x, in.y, cs.x, cs.y, ye, yo);
+                    const uint2 out = make_uint2(f32_canon(ye), f32_canon(yo));
+                    uint2* dst = static_cast<uint2*>(a.dst[x]) + pair;
+                    if constexpr (VERIFY) {
+                        const uint2 have = *dst;
+                        bad += (have.x != out.x || have.y != out.y) ? 1u : 0u;
+                    } else {
+                        *dst = out;
+                    }
                 }
             }
         }
@@ -363,7 +356,7 @@ __global__ void __launch_bounds__(kFastBlock) rope_fast(FastArgs a) {
         float y0, y1, y2, y3;
         rotate(__uint_as_float(x.x), __uint_as_float(x.y), c[0], s[0], y0, y1);
         rotate(__uint_as_float(x.z), __uint_as_float(x.w), c[1], s[1], y2, y3);
-        y = (u32x4){__float_as_uint(y0), __float_as_uint(y1), __float_as_uint(y2), __float_as_uint(y3)};
+        y = (u32x4){f32_canon(y0), f32_canon(y1), f32_canon(y2), f32_canon(y3)};
     }
     stream_store16(y, dst + blk * kFastBlock, kFastBlock * 16u, threadIdx.x * 16u);
 }
@@ -407,36 +400,36 @@ uint32_t elem_size(const Problem& p) { return p.dtype == LTX3DROPE_DTYPE_F32 ? 4
 
 PlainArgs plain_args(const Problem& p, unsigned* mismatches) {
     PlainArgs a;
-    a.q = p.q;
-    a.k = p.k;
-    a.q_out = p.q_out;
-    a.k_out = p.k_out;
+    a.src[0] = p.q;
+    a.src[1] = p.k;
+    a.dst[0] = p.q_out;
+    a.dst[1] = p.k_out;
     a.tab = reinterpret_cast<const float2*>(p.tab);
     a.mismatches = mismatches;
-    const uint64_t numel = uint64_t(p.B) * p.T * p.H * p.W * p.heads * p.D;
-    a.pairs = static_cast<uint32_t>(numel / 2);
-    a.pph = p.D / 2;
+    a.rows = p.B * p.T * p.H * p.W * p.heads;  // < 2^31 (fewer than 2^32 elements, head_dim >= 2)
     a.heads = p.heads;
-    a.N = p.T * p.H * p.W;
-    a.HW = p.H * p.W;
+    a.half_dim = p.D / 2;
+    a.T = p.T;
+    a.H = p.H;
     a.W = p.W;
-    a.PT = p.PT;
-    a.PH = p.PH;
-    a.PW = p.PW;
-    a.offH = p.tabT * p.PT;
-    a.offW = p.tabT * p.PT + p.tabH * p.PH;
-    a.t_off = p.t_off;
-    a.h_off = p.h_off;
-    a.w_off = p.w_off;
+    a.origin[0] = p.t_off;
+    a.origin[1] = p.h_off;
+    a.origin[2] = p.w_off;
+    a.width[0] = p.PT;
+    a.width[1] = p.PH;
+    a.width[2] = p.PW;
+    a.section[0] = 0;
+    a.section[1] = p.tabT * p.PT;
+    a.section[2] = p.tabT * p.PT + p.tabH * p.PH;
     return a;
 }
 
 template <bool VERIFY>
 hipError_t launch_plain_impl(const Problem& p, unsigned* mismatches, hipStream_t stream, int device) {
     const PlainArgs a = plain_args(p, mismatches);
-    const uint32_t want = (a.pairs + kPlainBlock - 1) / kPlainBlock;
-    const uint32_t cap = static_cast<uint32_t>(cu_count(device)) * 32u;
-    const uint32_t blocks = want < cap ? want : cap;
+    const uint64_t want = (2ull * a.rows + kPlainBlock - 1) / kPlainBlock;
+    const uint64_t cap = static_cast<uint64_t>(cu_count(device)) * 32u;
+    const uint32_t blocks = static_cast<uint32_t>(want < cap ? want : cap);
     if (blocks == 0) return hipSuccess;
     if (p.dtype == LTX3DROPE_DTYPE_BF16)
         hipLaunchKernelGGL((rope_plain<true, VERIFY>), dim3(blocks), dim3(kPlainBlock), 0, stream, a);

@@ -57,6 +57,7 @@ hipError_t hipSetDevice(int d) {
     return d == 0 ? hipSuccess : hipErrorInvalidDevice;
 }
 hipError_t hipGetLastError() { return hipSuccess; }
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus*) { return refuse(); }
 hipError_t hipDeviceGetAttribute(int*, hipDeviceAttribute_t, int) { return refuse(); }
 hipError_t hipPointerGetAttributes(hipPointerAttribute_t*, const void*) { return refuse(); }
 hipError_t hipMemGetAddressRange(hipDeviceptr_t*, size_t*, hipDeviceptr_t) { return refuse(); }

@@ -118,3 +118,24 @@ def test_only_the_cpu_leg_runs_the_oracle():
                 assert fn.name.startswith("cpu_leg_") or fn.name in allowed, fn.name
     top = [n for n in tree.body if isinstance(n, (ast.Import, ast.ImportFrom))]
     assert not any("oracle" in ast.dump(n) for n in top)
+
+
+def test_cpu_leg_compares_every_element():
+    """The bench line's parity pass: the oracle over blocks of rows of every frame, compared with a
+    result bit for bit -- the oracle's own output passes, and each planted difference is counted."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    shape, split = (2, 3, 5, 7, 4, 32), (8, 8, 16)
+    for dtype in (oracle.BF16, oracle.F32):
+        q, _ = workloads.generate_custom(shape, dtype, seed=77)
+        want = oracle.rope3d(q, dtype, split)
+        assert bench.cpu_leg_compare_all(q, want, dtype, split, 10000.0, 3) == (0, None)
+        bad = want.copy()
+        raw = bad.view(np.uint32) if dtype == oracle.F32 else bad
+        raw[1, 2, 4, 6, 3, 31] ^= 1
+        raw[0, 0, 0, 0, 0, 0] ^= 2
+        n, first = bench.cpu_leg_compare_all(q, bad, dtype, split, 10000.0, 3)
+        assert n == 2 and first["index"] == [0, 0, 0, 0, 0, 0]

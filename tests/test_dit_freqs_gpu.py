@@ -56,11 +56,14 @@ def test_grid_kernel_through_the_c_abi():
     np.testing.assert_array_equal(buf[:n].cpu().numpy().view(np.uint32),
                                   df.freq_grid(10000.0, 4096, 6, True).view(np.uint32))
     assert bool((buf[n:] == -3.0).all())
-    # an allocation too small for the grid, and host memory, are refused before any launch
+    # an allocation too small for the grid, and host memory, are refused before any launch: 2^22
+    # values (16 MiB) do not fit in the 2 MiB small-block segment of torch's allocator that holds
+    # an 8-float tensor (the library sees allocations, not tensors)
     small = torch.empty(8, dtype=torch.float32, device=DEV)
-    assert L.ltx3drope_dit_freq_grid(10000.0, 4096, 6, 1, small.data_ptr(), None, None) == _lib.E_UNSUPPORTED
+    assert L.ltx3drope_dit_freq_grid(10000.0, 1 << 22, 1, 1, small.data_ptr(), None, None) == _lib.E_UNSUPPORTED
     host = torch.empty(n, dtype=torch.float32).pin_memory()
     assert L.ltx3drope_dit_freq_grid(10000.0, 4096, 6, 1, host.data_ptr(), None, None) == _lib.E_UNSUPPORTED
+    torch.cuda.synchronize()
 
 
 def test_grid_kernel_repeated_calls_identical():

@@ -1,10 +1,12 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle, bit for bit.
 
-Tolerance is 0 ULP for every finite value (NaN compared by class).  Small and
-ragged shapes are compared element by element in full; the full-size workloads
-are compared on sampled tokens (every head and channel of each sampled token)
-plus properties that hold at any size: fast kernel == plain kernel on the whole
-output, unit-vector readback of the tables, untouched inputs and guard bands.
+Tolerance is 0 ULP on the raw bits of every element (NaN results are the
+canonical quiet NaN on both sides).  Every output is compared element by element
+with the oracle: small, ragged and random shapes, and the full-size workloads
+(the oracle runs over blocks of each frame in a thread pool, tests/oracle_full.py),
+up to the largest tensors the op takes.  Properties that hold at any size are
+checked besides: fast kernel == plain kernel on the whole output, unit-vector
+readback of the tables, untouched inputs and guard bands.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ import torch
 
 import oracle
 import workloads
+from tests import oracle_full
 
 pytestmark = pytest.mark.gpu
 
@@ -71,10 +74,6 @@ def assert_bitexact(got: np.ndarray, want: np.ndarray, dtype: str, what: str):
     assert got.shape == want.shape, (what, got.shape, want.shape)
     g, w = bits(got), bits(want)
     neq = g != w
-    if neq.any():
-        gf, wf = oracle.to_f32(got, dtype), oracle.to_f32(want, dtype)
-        both_nan = np.isnan(gf) & np.isnan(wf)
-        neq &= ~both_nan
     n = int(neq.sum())
     if n:
         idx = np.argwhere(neq)[:5]
@@ -272,12 +271,12 @@ def test_special_values(dtype):
 # full-size workloads: sampled tokens against the oracle, fast == plain in full
 # ---------------------------------------------------------------------------
 
-def sampled_check(x_host, out_dev, w, grid_index, count, seed):
-    B, T, H, W, heads, D = w.shape(grid_index)
-    ids = workloads.sample_tokens(B * T * H * W, count, seed)
-    want = oracle.rope3d_sampled(x_host, w.dtype, w.split, ids, w.base)
-    got = to_host(out_dev.view(B * T * H * W, heads, D)[torch.from_numpy(ids).to(DEV)], w.dtype)
-    assert_bitexact(got, want, w.dtype, f"workload {w.key} grid {grid_index} sampled tokens")
+def full_check(x_host, out_dev, dtype, split, base, what):
+    """Every element of out_dev against the oracle applied to x_host (raw bits)."""
+    got = to_host(out_dev, dtype)
+    n, first = oracle_full.compare_full(x_host, got, dtype, split, base)
+    log(f"{what}: {x_host.size} elements compared with the oracle, {n} differ")
+    assert n == 0, f"{what}: {n} of {x_host.size} elements differ from the oracle, first {first}"
 
 
 def fast_equals_plain(dq, dk, qo, ko, split, base):
@@ -307,9 +306,8 @@ def test_workload3_24_calls_one_table_set():
     for qo, ko in outs[1:]:
         assert torch.equal(qo.view(torch.int16), q0.view(torch.int16))
         assert torch.equal(ko.view(torch.int16), k0.view(torch.int16))
-    log("workload 3: sampled oracle comparison")
-    sampled_check(q, q0, w, 0, 3000, seed=30)
-    sampled_check(k, k0, w, 0, 3000, seed=31)
+    full_check(q, q0, w.dtype, w.split, w.base, "workload 3 q")
+    full_check(k, k0, w.dtype, w.split, w.base, "workload 3 k")
     fast_equals_plain(dq, dk, q0, k0, w.split, w.base)
 
 
@@ -320,27 +318,22 @@ def test_workload4_outliers():
     assert (oracle.to_f32(q[..., :64], w.dtype) == 60.0).any() and (oracle.to_f32(k[..., :64], w.dtype) == -60.0).any()
     dq, dk = to_dev(q, w.dtype), to_dev(k, w.dtype)
     qo, ko = run(dq, dk, w.split, w.base)
-    log("workload 4: sampled oracle comparison")
-    sampled_check(q, qo, w, 0, 3000, seed=40)
-    sampled_check(k, ko, w, 0, 3000, seed=41)
+    full_check(q, qo, w.dtype, w.split, w.base, "workload 4 q")
+    full_check(k, ko, w.dtype, w.split, w.base, "workload 4 k")
     fast_equals_plain(dq, dk, qo, ko, w.split, w.base)
 
 
 def test_fp32_at_workload4_size():
     """The fp32 fast kernel (two pairs per vector) at full size: workload 4's geometry in fp32
-    (1.8 GB per tensor), sampled tokens against the oracle and fast == plain over the whole output."""
+    (1.8 GB per tensor), every element against the oracle and fast == plain over the whole output."""
     shape, split = (1, 16, 96, 96, 24, 128), (32, 48, 48)
     log("fp32 at workload 4 size: generating inputs")
     q, k = workloads.generate_custom(shape, oracle.F32, seed=44)
     dq, dk = to_dev(q, oracle.F32), to_dev(k, oracle.F32)
     qo, ko = run(dq, dk, split)
     assert rla.stats()["fast_launches"] >= 1 and rla.stats()["gate_disabled"] == 0
-    B, T, H, W, heads, D = shape
-    for x, out, seed in ((q, qo, 42), (k, ko, 43)):
-        ids = workloads.sample_tokens(B * T * H * W, 2000, seed)
-        want = oracle.rope3d_sampled(x, oracle.F32, split, ids)
-        got = to_host(out.view(B * T * H * W, heads, D)[torch.from_numpy(ids).to(DEV)], oracle.F32)
-        assert_bitexact(got, want, oracle.F32, "fp32 workload-4 geometry, sampled tokens")
+    full_check(q, qo, oracle.F32, split, 10000.0, "fp32 at workload 4 size q")
+    full_check(k, ko, oracle.F32, split, 10000.0, "fp32 at workload 4 size k")
     del q, k
     fast_equals_plain(dq, dk, qo, ko, split, 10000.0)
 
@@ -365,9 +358,8 @@ def test_workload5_three_alternating_grids():
     assert (s["cache_misses"], s["cache_hits"], s["cache_evictions"]) == (3, 9, 0)
     assert s["gate_verifications"] == 3 and s["gate_trusted"] == 3
     for gi in range(3):
-        log(f"workload 5 grid {gi}: sampled oracle comparison")
-        sampled_check(data[gi][0], results[gi][0], w, gi, 1500, seed=50 + gi)
-        sampled_check(data[gi][1], results[gi][1], w, gi, 1500, seed=60 + gi)
+        full_check(data[gi][0], results[gi][0], w.dtype, w.split, w.base, f"workload 5 grid {gi} q")
+        full_check(data[gi][1], results[gi][1], w.dtype, w.split, w.base, f"workload 5 grid {gi} k")
         fast_equals_plain(dev[gi][0], dev[gi][1], results[gi][0], results[gi][1], w.split, w.base)
 
 
@@ -611,7 +603,8 @@ def test_frame_shards_of_workload4_match_the_full_result():
             assert torch.equal(oq.view(torch.int16), fq[:, sl].view(torch.int16)), r
             assert torch.equal(ok.view(torch.int16), fk[:, sl].view(torch.int16)), r
     torch.cuda.synchronize()
-    sampled_check(q, fq, w, 0, 1000, seed=45)
+    full_check(q, fq, w.dtype, w.split, w.base, "workload 4 (unsharded reference of the shards) q")
+    full_check(k, fk, w.dtype, w.split, w.base, "workload 4 (unsharded reference of the shards) k")
     # a spatial tile as well: rows 32..63, columns 64..95 of every frame
     with rla.tables_build(*w.grids[0], w.split, w.base) as tab:
         tq = dq[:, :, 32:64, 64:96].contiguous()
@@ -652,11 +645,9 @@ def test_inplace_matches_out_of_place_and_respects_the_gate(dtype):
 def test_largest_supported_tensor():
     """31 heads x [1, 16, 64, 1024] x head_dim 128 = 4,160,749,568 elements per tensor (7.75 GiB of
     bf16), just under the 2^32 limit: the gate's full-size verification, fast == plain over the
-    whole output, sampled tokens (the last included) against the oracle; one more head (2^32
-    elements) is refused without a launch.  Inputs are finite random bf16 patterns drawn on the
-    device."""
+    whole output, and every element of Q and K against the oracle; one more head (2^32 elements)
+    is refused without a launch.  Inputs are finite random bf16 patterns drawn on the device."""
     shape, split = (1, 16, 64, 1024, 31, 128), (32, 48, 48)
-    N, heads, D = 16 * 64 * 1024, 31, 128
     log("largest tensor: generating inputs on the device")
     dq = workloads.generate_bf16_bits(shape, 101, DEV)
     dk = workloads.generate_bf16_bits(shape, 102, DEV)
@@ -675,11 +666,6 @@ def test_largest_supported_tensor():
         assert torch.equal(qo.view(torch.int16), pq.view(torch.int16))
         assert torch.equal(ko.view(torch.int16), pk.view(torch.int16))
         del pq, pk
-    log("largest tensor: sampled oracle comparison")
-    tabs = oracle.grid_tables(16, 64, 1024, split, 10000.0)
-    for x, out, seed in ((dq, qo, 90), (dk, ko, 91)):
-        ids = workloads.sample_tokens(N, 800, seed)
-        idx = torch.from_numpy(ids).to(DEV)
-        rows = to_host(x.view(N, heads, D)[idx], oracle.BF16)
-        want = oracle.apply_rope_tokens(rows, oracle.BF16, oracle.token_coords(ids, 16, 64, 1024), tabs, split)
-        assert_bitexact(to_host(out.view(N, heads, D)[idx], oracle.BF16), want, oracle.BF16, "sampled tokens")
+    log("largest tensor: oracle comparison of every element")
+    for x, out, name in ((dq, qo, "q"), (dk, ko, "k")):
+        full_check(to_host(x, oracle.BF16), out, oracle.BF16, split, 10000.0, f"largest tensor {name}")

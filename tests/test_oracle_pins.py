@@ -273,6 +273,29 @@ def pin_bf16_cast():
     assert orc.f32_to_bf16_bits(np.array([-np.inf], np.float32))[0] == 0xFF80
 
 
+def pin_nan_canonical():
+    """A NaN result is the canonical quiet NaN in both dtypes (0x7FC00000, 0x7FC0), whatever the
+    sign and payload of the NaN that caused it; an infinity times a zero table entry (sin 0 at
+    position 0) is a NaN too.  Every other element is untouched by the rule."""
+    shape, split = (1, 2, 2, 2, 1, 12), (4, 4, 4)
+    rng = np.random.Generator(np.random.PCG64(41))
+    n = int(np.prod(shape))
+    idx = rng.choice(n, 24, replace=False)
+    f32 = rng.standard_normal(n).astype(np.float32)
+    f32.view(np.uint32)[idx] = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF812345, 0x7FFFFFFF, 0x7FA00000],
+                                        np.uint32)[np.arange(24) % 6]
+    bf = orc.f32_to_bf16_bits(rng.standard_normal(n).astype(np.float32))
+    bf[idx] = np.array([0x7FC0, 0xFFC0, 0x7F81, 0xFF92, 0x7FFF, 0xFFA3], np.uint16)[np.arange(24) % 6]
+    for dtype, x, canon in ((oracle.F32, f32, 0x7FC00000), (oracle.BF16, bf, 0x7FC0)):
+        x = x.reshape(shape).copy()
+        x.reshape(-1)[1] = np.float32(np.inf) if dtype == oracle.F32 else np.uint16(0x7F80)  # odd element, origin
+        out = orc.rope3d(x, dtype, split, BASE)
+        raw = out.view(np.uint32) if dtype == oracle.F32 else out
+        nan = np.isnan(orc.to_f32(out, dtype))
+        assert nan.sum() >= 24 and nan.reshape(-1)[0], int(nan.sum())
+        assert np.all(raw[nan] == canon), [hex(v) for v in raw[nan][:4]]
+
+
 ALL_PINS = [
     ("inv_freq", pin_inv_freq_closed_forms),
     ("tables_exact", lambda: (pin_tables_exact(4, 16), pin_tables_exact(5, 24), pin_tables_exact(3, 12))),
@@ -287,6 +310,7 @@ ALL_PINS = [
     ("bf16_cast", pin_bf16_cast),
     ("brute_shard", lambda: pin_brute_force((1, 2, 2, 3, 1, 12), oracle.BF16, (4, 4, 4), 25, offsets=(3, 1, 2))),
     ("shard_slab", lambda: pin_shard_is_slab_of_full((2, 6, 5, 7, 2, 24), (8, 8, 8), (2, 1, 3), (3, 3, 4), 26)),
+    ("nan_canonical", pin_nan_canonical),
 ]
 
 
@@ -396,6 +420,10 @@ def test_bf16_cast_against_torch_and_closed_forms():
     pin_bf16_cast()
 
 
+def test_nan_results_are_canonical():
+    pin_nan_canonical()
+
+
 def test_validate_rejects_page_rules():
     with pytest.raises(ValueError):
         orc.validate((1, 2, 3, 4, 5), (2, 2, 2))
@@ -493,6 +521,13 @@ def _rope3d_offsets_rotated(x, dtype, split, base=10000.0, tables=None, offsets=
                                         (h0 + T <= g[0] and w0 + H <= g[1] and t0 + W <= g[2]) else (0, 0, 0), g)
 
 
+def _from_f32_keeps_nan_payload(y, dtype):
+    if dtype == oracle.BF16:
+        u = np.ascontiguousarray(y, dtype=np.float32).view(np.uint32).astype(np.uint64)
+        return ((u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)).astype(np.uint16)
+    return np.asarray(y, dtype=np.float32)
+
+
 MUTATIONS = [
     ("rotate_pairs", _rot_sign_flip),
     ("rotate_pairs", _rot_swap_cs),
@@ -507,6 +542,7 @@ MUTATIONS = [
     ("axis_tables", _axis_tables_off_by_one),
     ("rope3d", _rope3d_offsets_ignored),
     ("rope3d", _rope3d_offsets_rotated),
+    ("from_f32", _from_f32_keeps_nan_payload),
 ]
 
 
