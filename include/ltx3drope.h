@@ -201,6 +201,26 @@ int ltx3drope_apply_qk(void* q_out, void* k_out, const void* q, const void* k, i
                        ltx3drope_tables_t tables, void* stream);
 
 /*
+ * ltx3drope_apply_qk_noalloc - ltx3drope_apply_qk for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, precheck, kernels, gate and results as ltx3drope_apply_qk (the caller passes
+ * the inputs and the outputs), but it calls no hipMalloc, hipFree or other allocating routine:
+ * the gate's verification counts its mismatches in a static 256-byte device array of the
+ * library (one copy per GPU, held until the process ends) instead of the counter block
+ * ltx3drope_apply_qk allocates on a device's first verification.  The counter is cleared by a
+ * kernel before each use; its size does not depend on the input, so every input the precheck
+ * accepts (fewer than 2^32 elements per tensor) fits.  Every call on one GPU shares that array,
+ * which keeps the last call's contents: verifications on one GPU are serialized by a host mutex
+ * of the library from the counter's clearing to its read-back, and calls that overlap on one GPU
+ * without it (from outside the library) would race.  The tables come from
+ * ltx3drope_tables_build beforehand (which does allocate, once per grid).  E_UNSUPPORTED also for
+ * tables of device index 64 or above.
+ */
+int ltx3drope_apply_qk_noalloc(void* q_out, void* k_out, const void* q, const void* k, int dtype,
+                               int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
+                               ltx3drope_tables_t tables, void* stream);
+
+/*
  * Shards.  A sequence- or tile-parallel rank holds a slab of a larger token
  * grid; its tokens must take the table rows of their global coordinates.
  * (Positions on the page are tile-local because the table cache key carries

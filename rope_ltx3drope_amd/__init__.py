@@ -33,6 +33,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "Ltx3dRopeError", "Ltx3dRopeUnsupported", "Tables", "tables", "tables_build", "can_use", "apply_qk",
+    "apply_qk_noalloc",
     "forward_pair", "kernel_choice", "stats", "stats_reset", "set_option", "get_option", "gate_state", "gate_reset",
     "cache_clear", "copy_bytes", "version", "neox_can_use", "neox_apply_qk", "neox_position_errors", "patchify",
     "unpatchify", "dit_freq_grid",
@@ -245,6 +246,23 @@ def apply_qk(q, k, tabs: Tables, q_out=None, k_out=None, stream=None, offsets=No
             _lib.lib().ltx3drope_can_use_shard(*args, ctypes.byref(sh), tabs.handle, ctypes.byref(reason))
         raise Ltx3dRopeUnsupported(_lib.REASONS.get(reason.value, str(reason.value)), st)
     _check(st, "apply_qk")
+    return q_out, k_out
+
+
+def apply_qk_noalloc(q, k, tabs: Tables, q_out, k_out, stream=None):
+    """apply_qk into caller-provided outputs through the entry point that allocates no device memory
+    (the gate's verification counter is a static device array of the library)."""
+    B, T, H, W, heads, D = _shape6(q)
+    if q_out is None or k_out is None:
+        raise ValueError("apply_qk_noalloc writes into caller-provided q_out and k_out")
+    _marshal(q, k, q_out, k_out)
+    args = (q_out.data_ptr(), k_out.data_ptr(), q.data_ptr(), k.data_ptr(), _dtype_code(q), B, T, H, W, heads, D)
+    st = _lib.lib().ltx3drope_apply_qk_noalloc(*args, tabs.handle, _stream_ptr(q.device, stream))
+    if st in (_lib.E_UNSUPPORTED, _lib.E_TABLE_MISMATCH):
+        reason = ctypes.c_int(0)
+        _lib.lib().ltx3drope_can_use(*args, tabs.handle, ctypes.byref(reason))
+        raise Ltx3dRopeUnsupported(_lib.REASONS.get(reason.value, str(reason.value)), st)
+    _check(st, "apply_qk_noalloc")
     return q_out, k_out
 
 

@@ -39,7 +39,8 @@ GATE_STATES = {0: "UNSEEN", 1: "TRUSTED", 2: "DISABLED"}
 # every symbol the header declares (checked by the CPU test suite)
 EXPORTS = (
     "ltx3drope_tables_build", "ltx3drope_tables_release", "ltx3drope_tables_describe", "ltx3drope_tables_read",
-    "ltx3drope_cache_clear", "ltx3drope_can_use", "ltx3drope_apply_qk", "ltx3drope_can_use_shard",
+    "ltx3drope_cache_clear", "ltx3drope_can_use", "ltx3drope_apply_qk", "ltx3drope_apply_qk_noalloc",
+    "ltx3drope_can_use_shard",
     "ltx3drope_apply_qk_shard", "ltx3drope_neox_can_use", "ltx3drope_neox_apply_qk",
     "ltx3drope_neox_position_errors", "ltx3drope_patchify", "ltx3drope_unpatchify", "ltx3drope_dit_freq_grid",
     "ltx3drope_gate_state",
@@ -105,6 +106,8 @@ def lib() -> ctypes.CDLL:
             "ltx3drope_can_use": (ctypes.c_int, [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64, vp,
                                                  ctypes.POINTER(ctypes.c_int)]),
             "ltx3drope_apply_qk": (ctypes.c_int, [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64, vp, vp]),
+            "ltx3drope_apply_qk_noalloc": (ctypes.c_int, [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64,
+                                                          vp, vp]),
             "ltx3drope_can_use_shard": (ctypes.c_int, [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64,
                                                        ctypes.POINTER(Shard), vp, ctypes.POINTER(ctypes.c_int)]),
             "ltx3drope_apply_qk_shard": (ctypes.c_int, [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64,

@@ -286,22 +286,40 @@ int run_kernel(Kernel which, const Problem& p, hipStream_t stream, int device) {
     return LTX3DROPE_OK;
 }
 
+// Verifications of the no-allocation entry point, one at a time per device: they share that
+// device's static scratch counter.
+std::mutex g_noalloc_verify_mu[kMaxDevices];
+
 // Fast kernel into the outputs, then the plain kernel re-derives every pair on the
 // device and counts disagreements.  Returns a status; *equal receives the verdict.
-int verify_fast(const Problem& p, hipStream_t stream, int device, bool* equal) {
-    DeviceRes* res = nullptr;
-    int st = device_res(device, &res);
+// The counter is the device's allocated counter block, or (noalloc) the library's
+// static device scratch; either way one verification at a time per device uses it,
+// from its clearing to its read-back.
+int verify_fast(const Problem& p, hipStream_t stream, int device, bool noalloc, bool* equal) {
+    unsigned* counter = nullptr;
+    std::mutex* mu = nullptr;
+    if (noalloc) {
+        if (device < 0 || device >= kMaxDevices) return LTX3DROPE_E_INVALID;
+        if (scratch_counter(device, &counter) != hipSuccess) {
+            (void)hipGetLastError();
+            return LTX3DROPE_E_HIP;
+        }
+        mu = &g_noalloc_verify_mu[device];
+    } else {
+        DeviceRes* res = nullptr;
+        const int st = device_res(device, &res);
+        if (st != LTX3DROPE_OK) return st;
+        counter = res->counter;
+        mu = &res->verify_mu;
+    }
+    std::lock_guard<std::mutex> lock(*mu);
+    int st = run_kernel(Kernel::Fast, p, stream, device);
     if (st != LTX3DROPE_OK) return st;
-    // held until the count is back on the host, so concurrent first calls (other threads, other
-    // streams) cannot clear or add to this verification's counter
-    std::lock_guard<std::mutex> lock(res->verify_mu);
-    st = run_kernel(Kernel::Fast, p, stream, device);
-    if (st != LTX3DROPE_OK) return st;
-    if (launch_zero_u32(res->counter, stream) != hipSuccess) return LTX3DROPE_E_HIP;
-    if (launch_verify(p, res->counter, stream, device) != hipSuccess || hipGetLastError() != hipSuccess)
+    if (launch_zero_u32(counter, stream) != hipSuccess) return LTX3DROPE_E_HIP;
+    if (launch_verify(p, counter, stream, device) != hipSuccess || hipGetLastError() != hipSuccess)
         return LTX3DROPE_E_HIP;
     unsigned host_count = 0;
-    if (hipMemcpyAsync(&host_count, res->counter, sizeof(unsigned), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+    if (hipMemcpyAsync(&host_count, counter, sizeof(unsigned), hipMemcpyDeviceToHost, stream) != hipSuccess ||
         hipStreamSynchronize(stream) != hipSuccess) {
         (void)hipGetLastError();
         return LTX3DROPE_E_HIP;
@@ -335,7 +353,7 @@ namespace {
 
 int apply_impl(void* q_out, void* k_out, const void* q, const void* k, int dtype, int64_t B, int64_t T, int64_t H,
                int64_t W, int64_t heads, int64_t head_dim, ltx3drope_tables_t tables, void* stream_ptr,
-               const Placement& pl) {
+               const Placement& pl, bool noalloc) {
     if (tables != nullptr && tables->host) {
         stats().rejected.fetch_add(1);
         return LTX3DROPE_E_UNSUPPORTED;
@@ -376,7 +394,7 @@ int apply_impl(void* q_out, void* k_out, const void* q, const void* k, int dtype
     if (capture != hipStreamCaptureStatusNone) return run_kernel(Kernel::Plain, p, stream, device);
 
     bool equal = false;
-    const int st = verify_fast(p, stream, device, &equal);
+    const int st = verify_fast(p, stream, device, noalloc, &equal);
     if (st != LTX3DROPE_OK) return st;
     if (equal) {
         if (state != LTX3DROPE_GATE_TRUSTED) stats().trusted.fetch_add(1);
@@ -570,7 +588,17 @@ int ltx3drope_kernel_choice(const void* q_out, const void* k_out, const void* q,
 int ltx3drope_apply_qk(void* q_out, void* k_out, const void* q, const void* k, int dtype, int64_t B, int64_t T,
                        int64_t H, int64_t W, int64_t heads, int64_t head_dim, ltx3drope_tables_t tables,
                        void* stream_ptr) {
-    return apply_impl(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, stream_ptr, Placement());
+    return apply_impl(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, stream_ptr, Placement(), false);
+}
+
+int ltx3drope_apply_qk_noalloc(void* q_out, void* k_out, const void* q, const void* k, int dtype, int64_t B,
+                               int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
+                               ltx3drope_tables_t tables, void* stream_ptr) {
+    if (tables != nullptr && (tables->device < 0 || tables->device >= kMaxDevices)) {
+        stats().rejected.fetch_add(1);
+        return LTX3DROPE_E_UNSUPPORTED;
+    }
+    return apply_impl(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, stream_ptr, Placement(), true);
 }
 
 int ltx3drope_apply_qk_shard(void* q_out, void* k_out, const void* q, const void* k, int dtype, int64_t B, int64_t T,
@@ -581,7 +609,7 @@ int ltx3drope_apply_qk_shard(void* q_out, void* k_out, const void* q, const void
         stats().rejected.fetch_add(1);
         return LTX3DROPE_E_TABLE_MISMATCH;
     }
-    return apply_impl(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, stream_ptr, pl);
+    return apply_impl(q_out, k_out, q, k, dtype, B, T, H, W, heads, head_dim, tables, stream_ptr, pl, false);
 }
 
 int ltx3drope_neox_can_use(const void* q_out, const void* k_out, const void* q, const void* k, int dtype,

@@ -56,6 +56,13 @@ hipError_t launch_plain(const Problem& p, hipStream_t stream, int device);
 // from what q_out/k_out already hold (raw bit patterns).
 hipError_t launch_verify(const Problem& p, unsigned* mismatches, hipStream_t stream, int device);
 hipError_t launch_zero_u32(unsigned* ptr, hipStream_t stream);
+
+// The no-allocation entry point's device scratch (kernels.hip): a static 256-byte array per GPU,
+// word 0 the gate's mismatch counter.  scratch_counter() returns its device address on `device`,
+// which must be the current device (looked up once per device and kept).
+constexpr int kScratchWords = 64;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_counter(int device, unsigned** out);
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream, int device);
 
 // The rotate-half RoPE with a gathered cos/sin cache (neox.hip).

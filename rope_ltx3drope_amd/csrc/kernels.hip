@@ -440,6 +440,32 @@ hipError_t launch_plain_impl(const Problem& p, unsigned* mismatches, hipStream_t
 
 }  // namespace
 
+// Device scratch of the no-allocation entry point (ltx3drope_apply_qk_noalloc): word 0 is the gate
+// verification's mismatch counter.  Each GPU the library runs on holds its own copy until the
+// process ends.  Host code must not pass this name to a kernel (on the host it is only a stand-in
+// for the symbol): scratch_counter() returns the device address, looked up once per device.
+static __device__ __align__(256) unsigned scratch[kScratchWords];
+
+namespace {
+std::mutex g_scratch_mu;
+unsigned* g_scratch_addr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_counter(int device, unsigned** out) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[device] == nullptr) {
+        int current = -1;
+        if (hipGetDevice(&current) != hipSuccess || current != device) return hipErrorInvalidDevice;
+        void* addr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));  // this device's copy
+        if (e != hipSuccess || addr == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+        g_scratch_addr[device] = static_cast<unsigned*>(addr);
+    }
+    *out = g_scratch_addr[device];
+    return hipSuccess;
+}
+
 bool fast_supported(const Problem& p) {
     const uint32_t es = elem_size(p);
     for (const void* ptr : {static_cast<const void*>(p.q), static_cast<const void*>(p.k),

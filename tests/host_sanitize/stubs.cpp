@@ -76,4 +76,5 @@ hipError_t launch_neox_plain(const NeoxProblem&, unsigned*, hipStream_t, int) { 
 bool patch_fast_supported(const PatchProblem&) { return g_hip_calls.fetch_add(1), false; }
 hipError_t launch_patch(const PatchProblem&, bool, hipStream_t, int) { return refuse(); }
 hipError_t launch_dit_freqs(float*, uint32_t, double, bool, hipStream_t) { return refuse(); }
+hipError_t scratch_counter(int, unsigned**) { return refuse(); }
 }  // namespace ltx3drope
