@@ -16,12 +16,13 @@
 // coordinate, with token n = (t*H + h)*W + w in each batch element.
 //
 // Two kernels compute it:
-//  * rope_plain: one thread per (token, head) row of Q or of K, written from
-//    the eager definition: the thread finds its token's (t, h, w) from the
-//    row's place in the contiguous [B, T, H, W, heads, head_dim] layout, then
-//    walks the time, height and width chunks of the row in turn, rotating each
-//    chunk's pairs with the table row of that axis's coordinate; scalar loads
-//    and stores, integer round-to-nearest-even.  It is the reference path of
+//  * rope_plain: one wavefront per (token, head) row of Q or of K, written
+//    from the eager definition: the row's token (t, h, w) is peeled from its
+//    place in the contiguous [B, T, H, W, heads, head_dim] layout; the lanes
+//    spread over the row's pairs, each finding its chunk (time, height, width)
+//    by walking the chunk widths, and rotating its pair with the table row of
+//    that axis's coordinate; scalar loads and stores, integer
+//    round-to-nearest-even.  It is the reference path of
 //    the bit-exact gate and the fallback for shapes the fast kernel does not
 //    cover.  With VERIFY it recomputes the result and counts pairs whose bits
 //    differ from what the outputs already hold.
@@ -95,7 +96,7 @@ __device__ __forceinline__ uint32_t bf16_pack_hw(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------
-// plain kernel: one (token, head) row per thread
+// plain kernel: one (token, head) row per wavefront
 // ---------------------------------------------------------------------------
 
 struct PlainArgs {
@@ -113,11 +114,14 @@ struct PlainArgs {
 
 template <bool BF16, bool VERIFY>
 __global__ void __launch_bounds__(kPlainBlock) rope_plain(PlainArgs a) {
+    constexpr uint32_t kWaves = kPlainBlock / 64;
     uint32_t bad = 0;
+    const uint32_t lane = threadIdx.x % 64;
     // 2 * rows < 2^32 (a tensor holds fewer than 2^32 elements, a row at least 2); the index is
-    // 64-bit so that adding the grid stride cannot wrap
+    // 64-bit so that adding the grid's stride cannot wrap
     const uint64_t items = 2ull * a.rows;
-    for (uint64_t item = blockIdx.x * kPlainBlock + threadIdx.x; item < items; item += gridDim.x * kPlainBlock) {
+    const uint64_t stride = uint64_t(gridDim.x) * kWaves;
+    for (uint64_t item = uint64_t(blockIdx.x) * kWaves + threadIdx.x / 64; item < items; item += stride) {
         const uint32_t x = item < a.rows ? 0 : 1;  // 0: Q, 1: K
         const uint32_t row = static_cast<uint32_t>(item - x * uint64_t(a.rows));
         // row = ((((b*T + t)*H + h)*W + w)*heads + head: peel the layout from the innermost axis out
@@ -128,33 +132,35 @@ __global__ void __launch_bounds__(kPlainBlock) rope_plain(PlainArgs a) {
         coord[1] = rest % a.H;
         rest /= a.H;
         coord[0] = rest % a.T;
-        uint32_t pair = row * a.half_dim;  // first (even, odd) pair of the row; < 2^31
-        for (int axis = 0; axis < 3; ++axis) {
-            const float2* cs_row = a.tab + a.section[axis] + (coord[axis] + a.origin[axis]) * a.width[axis];
-            for (uint32_t i = 0; i < a.width[axis]; ++i, ++pair) {
-                const float2 cs = cs_row[i];
-                float ye, yo;
-                if constexpr (BF16) {
-                    const uint32_t in = static_cast<const uint32_t*>(a.src[x])[pair];
-                    rotate(bf16_lo(in), bf16_hi(in), cs.x, cs.y, ye, yo);
-                    const uint32_t out = bf16_rne_int(ye) | (bf16_rne_int(yo) << 16);
-                    uint32_t* dst = static_cast<uint32_t*>(a.dst[x]) + pair;
-                    if constexpr (VERIFY) {
-                        bad += *dst != out ? 1u : 0u;
-                    } else {
-                        *dst = out;
-                    }
+        const uint32_t first = row * a.half_dim;  // the row's first (even, odd) pair; < 2^31
+        for (uint32_t i = lane; i < a.half_dim; i += 64) {
+            // the chunk that holds pair i of the row: walk the t, h and w widths
+            int axis = 0;
+            uint32_t j = i;
+            while (axis < 2 && j >= a.width[axis]) j -= a.width[axis++];
+            const float2 cs = a.tab[a.section[axis] + (coord[axis] + a.origin[axis]) * a.width[axis] + j];
+            const uint32_t pair = first + i;
+            float ye, yo;
+            if constexpr (BF16) {
+                const uint32_t in = static_cast<const uint32_t*>(a.src[x])[pair];
+                rotate(bf16_lo(in), bf16_hi(in), cs.x, cs.y, ye, yo);
+                const uint32_t out = bf16_rne_int(ye) | (bf16_rne_int(yo) << 16);
+                uint32_t* dst = static_cast<uint32_t*>(a.dst[x]) + pair;
+                if constexpr (VERIFY) {
+                    bad += *dst != out ? 1u : 0u;
                 } else {
-                    const float2 in = static_cast<const float2*>(a.src[x])[pair];
-                    rotate(in.x, in.y, cs.x, cs.y, ye, yo);
-                    const uint2 out = make_uint2(f32_canon(ye), f32_canon(yo));
-                    uint2* dst = static_cast<uint2*>(a.dst[x]) + pair;
-                    if constexpr (VERIFY) {
-                        const uint2 have = *dst;
-                        bad += (have.x != out.x || have.y != out.y) ? 1u : 0u;
-                    } else {
-                        *dst = out;
-                    }
+                    *dst = out;
+                }
+            } else {
+                const float2 in = static_cast<const float2*>(a.src[x])[pair];
+                rotate(in.x, in.y, cs.x, cs.y, ye, yo);
+                const uint2 out = make_uint2(f32_canon(ye), f32_canon(yo));
+                uint2* dst = static_cast<uint2*>(a.dst[x]) + pair;
+                if constexpr (VERIFY) {
+                    const uint2 have = *dst;
+                    bad += (have.x != out.x || have.y != out.y) ? 1u : 0u;
+                } else {
+                    *dst = out;
                 }
             }
         }
@@ -427,7 +433,7 @@ PlainArgs plain_args(const Problem& p, unsigned* mismatches) {
 template <bool VERIFY>
 hipError_t launch_plain_impl(const Problem& p, unsigned* mismatches, hipStream_t stream, int device) {
     const PlainArgs a = plain_args(p, mismatches);
-    const uint64_t want = (2ull * a.rows + kPlainBlock - 1) / kPlainBlock;
+    const uint64_t want = (2ull * a.rows + kPlainBlock / 64 - 1) / (kPlainBlock / 64);  // one row per wavefront
     const uint64_t cap = static_cast<uint64_t>(cu_count(device)) * 32u;
     const uint32_t blocks = static_cast<uint32_t>(want < cap ? want : cap);
     if (blocks == 0) return hipSuccess;
