@@ -117,3 +117,38 @@ def test_patchify_graph_replays():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(y.cpu().numpy().view(np.uint16), pf.patchify(h, p))
         np.testing.assert_array_equal(back.cpu().numpy().view(np.uint16), h)
+
+
+@pytest.mark.parametrize("entry", ["apply_qk", "apply_qk_noalloc"])
+def test_unverified_configuration_under_capture_runs_the_plain_kernel(entry):
+    """A configuration's first call made under graph capture cannot run the gate's verification
+    (it waits for a count on the host): the captured call is the plain kernel and the gate stays
+    UNSEEN.  Its replays are bit-exact; a later eager call verifies and trusts the fast kernel."""
+    shape, split = (1, 3, 8, 8, 12, 64), (16, 24, 24)
+    sets = [workloads.generate_custom(shape, oracle.BF16, seed=80 + i) for i in range(3)]
+    dq, dk = bf16_dev(sets[0][0]), bf16_dev(sets[0][1])
+    qo, ko = torch.empty_like(dq), torch.empty_like(dk)
+    call = getattr(rla, entry)
+    with rla.tables_build(*shape[1:4], split) as tab:  # built eagerly: the build allocates and waits
+        torch.cuda.synchronize()
+        assert rla.gate_state(0, rla.DTYPE_BF16, shape, split) == "UNSEEN"
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(dq, dk, tab, qo, ko)
+        st = rla.stats()
+        assert st["gate_verifications"] == 0 and st["plain_launches"] == 1 and st["fast_launches"] == 0
+        assert rla.gate_state(0, rla.DTYPE_BF16, shape, split) == "UNSEEN"
+        for q, k in sets[1:] + sets[:1]:
+            dq.copy_(bf16_dev(q))
+            dk.copy_(bf16_dev(k))
+            qo.zero_()
+            ko.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            want_q, want_k = oracle.rope3d_qk(q, k, oracle.BF16, split)
+            np.testing.assert_array_equal(bf16_host(qo), want_q)
+            np.testing.assert_array_equal(bf16_host(ko), want_k)
+        call(dq, dk, tab, qo, ko)  # eager now: verified, trusted
+        torch.cuda.synchronize()
+        assert rla.gate_state(0, rla.DTYPE_BF16, shape, split) == "TRUSTED"
+        assert rla.stats()["gate_verifications"] == 1
