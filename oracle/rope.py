@@ -132,11 +132,11 @@ def rotate_pairs(even: np.ndarray, odd: np.ndarray, cos: np.ndarray, sin: np.nda
     """
     f = np.float32
     with np.errstate(over="ignore", invalid="ignore"):
-        even_cos = np.multiply(even, cos, dtype=f)
-        odd_sin = np.multiply(odd, sin, dtype=f)
-        even_sin = np.multiply(even, sin, dtype=f)
-        odd_cos = np.multiply(odd, cos, dtype=f)
-        return np.subtract(even_cos, odd_sin, dtype=f), np.add(even_sin, odd_cos, dtype=f)
+        t1 = np.multiply(even, cos, dtype=f)  # e c
+        t2 = np.multiply(odd, sin, dtype=f)   # o s
+        t3 = np.multiply(even, sin, dtype=f)  # e s
+        t4 = np.multiply(odd, cos, dtype=f)   # o c
+        return np.subtract(t1, t2, dtype=f), np.add(t3, t4, dtype=f)
 
 
 def validate(shape: Sequence[int], split: Sequence[int]) -> None:

@@ -64,10 +64,10 @@ constexpr int kPlainBlock = 256;
 // products, each rounded to fp32, then one rounded difference (even result)
 // and one rounded sum (odd result); nothing is fused.
 __device__ __forceinline__ void rotate(float e, float o, float c, float s, float& ye, float& yo) {
-    const float ec = __fmul_rn(e, c), os_ = __fmul_rn(o, s);
-    const float es = __fmul_rn(e, s), oc = __fmul_rn(o, c);
-    ye = __fsub_rn(ec, os_);
-    yo = __fadd_rn(es, oc);
+    const float m0 = __fmul_rn(e, c), m1 = __fmul_rn(o, s);
+    const float m2 = __fmul_rn(e, s), m3 = __fmul_rn(o, c);
+    ye = __fsub_rn(m0, m1);
+    yo = __fadd_rn(m2, m3);
 }
 
 // bf16 <-> fp32.  A 32-bit word holds one pair: the even element in the low half.
