@@ -160,8 +160,10 @@ int ltx3drope_cache_clear(void);
  * pointer or handle; dtype F32 or BF16; B, T, H, W, heads, head_dim > 0;
  * table split widths even and > 0 and summing to head_dim; tables built for
  * (T, H, W); every pointer aligned to one pair (8 B for F32, 4 B for BF16);
- * neither output overlapping an input or the other output; fewer than 2^32
- * elements per tensor (8 GiB of bf16, 16 GiB of fp32); all four pointers
+ * neither output overlapping an input or the other output; each size below
+ * 2^31, fewer than 2^32 elements per batch element (8 GiB of bf16, 16 GiB of
+ * fp32) and at most 2^48 in all (a tensor of 2^32 elements or more runs as
+ * several launches of whole batch elements); all four pointers
  * device memory of the tables'
  * device, each inside an allocation large enough for the whole tensor
  * (checked last, REASON_NOT_DEVICE_PTR then REASON_EXTENT; skipped in
@@ -209,7 +211,7 @@ int ltx3drope_apply_qk(void* q_out, void* k_out, const void* q, const void* k, i
  * library (one copy per GPU, held until the process ends) instead of the counter block
  * ltx3drope_apply_qk allocates on a device's first verification.  The counter is cleared by a
  * kernel before each use; its size does not depend on the input, so every input the precheck
- * accepts (fewer than 2^32 elements per tensor) fits.  Every call on one GPU shares that array,
+ * accepts fits.  Every call on one GPU shares that array,
  * which keeps the last call's contents: verifications on one GPU are serialized by a host mutex
  * of the library from the counter's clearing to its read-back, and calls that overlap on one GPU
  * without it (from outside the library) would race.  The tables come from

@@ -203,17 +203,19 @@ int precheck(const void* q_out, const void* k_out, const void* q, const void* k,
     const int nptr = check_outputs ? 4 : 2;
     for (int i = 0; i < nptr; ++i)
         if (reinterpret_cast<uintptr_t>(ptrs[i]) % pair) return LTX3DROPE_REASON_ALIGN;
-    // Index width: fewer than 2^32 elements per tensor, so the kernels' 32-bit indices hold every
-    // pair (< 2^31) and every 16-byte vector (< 2^30).  Each factor < 2^31 and the running
-    // product < 2^32 are checked before any product can overflow.
+    // Index width: fewer than 2^32 elements per batch element, so the kernels' 32-bit indices hold
+    // every pair (< 2^31) and every 16-byte vector (< 2^30) of a launch; a tensor of 2^32 elements
+    // or more runs as several launches of whole batch elements (apply_impl).  Each size < 2^31,
+    // the products checked before they can overflow; at most 2^48 elements in all.
     const int64_t lim = int64_t(1) << 32;
-    int64_t numel = 1;
-    for (int64_t f : {B, T, H, W, heads, D}) {
-        if (f >= (int64_t(1) << 31) || numel > lim / f) return LTX3DROPE_REASON_TOO_LARGE;
-        numel *= f;
+    int64_t per_batch = 1;
+    for (int64_t f : {T, H, W, heads, D}) {
+        if (f >= (int64_t(1) << 31) || per_batch > lim / f) return LTX3DROPE_REASON_TOO_LARGE;
+        per_batch *= f;
     }
-    if (numel >= lim) return LTX3DROPE_REASON_TOO_LARGE;
-    const size_t bytes = static_cast<size_t>(numel) * es;
+    if (per_batch >= lim || B >= (int64_t(1) << 31) || B > (int64_t(1) << 48) / per_batch)
+        return LTX3DROPE_REASON_TOO_LARGE;
+    const size_t bytes = static_cast<size_t>(B * per_batch) * es;
     if (check_outputs) {
         // every output/input and output/output overlap is refused, except exact in-place aliasing
         const bool q_inplace = pl.inplace && q_out == q;
@@ -279,11 +281,46 @@ struct DeviceGuard {
     }
 };
 
+// Batch elements per launch: all of them when the tensor holds fewer than 2^32 elements, else as
+// many whole batch elements as stay below 2^32 (the precheck keeps one below it).
+uint32_t batch_per_launch(const Problem& p) {
+    const uint64_t per_batch = uint64_t(p.T) * p.H * p.W * p.heads * p.D;
+    const uint64_t fit = ((uint64_t(1) << 32) - 1) / per_batch;
+    return static_cast<uint32_t>(fit >= p.B ? p.B : fit);
+}
+
+// The part of a problem made of batch elements [b0, b0 + count).
+Problem batch_slice(const Problem& p, uint32_t b0, uint32_t count) {
+    const size_t es = p.dtype == LTX3DROPE_DTYPE_F32 ? 4 : 2;
+    const size_t off = size_t(b0) * p.T * p.H * p.W * p.heads * p.D * es;
+    Problem c = p;
+    c.B = count;
+    c.q = static_cast<const char*>(p.q) + off;
+    c.k = static_cast<const char*>(p.k) + off;
+    c.q_out = static_cast<char*>(p.q_out) + off;
+    c.k_out = static_cast<char*>(p.k_out) + off;
+    return c;
+}
+
 int run_kernel(Kernel which, const Problem& p, hipStream_t stream, int device) {
-    const hipError_t e = which == Kernel::Fast ? launch_fast(p, stream, device) : launch_plain(p, stream, device);
-    if (e != hipSuccess || hipGetLastError() != hipSuccess) return LTX3DROPE_E_HIP;
-    (which == Kernel::Fast ? stats().fast : stats().plain).fetch_add(1);
+    const uint32_t step = batch_per_launch(p);
+    for (uint32_t b0 = 0; b0 < p.B; b0 += step) {
+        const Problem c = batch_slice(p, b0, p.B - b0 < step ? p.B - b0 : step);
+        const hipError_t e = which == Kernel::Fast ? launch_fast(c, stream, device) : launch_plain(c, stream, device);
+        if (e != hipSuccess || hipGetLastError() != hipSuccess) return LTX3DROPE_E_HIP;
+        (which == Kernel::Fast ? stats().fast : stats().plain).fetch_add(1);
+    }
     return LTX3DROPE_OK;
+}
+
+hipError_t run_verify(const Problem& p, unsigned* counter, hipStream_t stream, int device) {
+    const uint32_t step = batch_per_launch(p);
+    for (uint32_t b0 = 0; b0 < p.B; b0 += step) {
+        const hipError_t e =
+            launch_verify(batch_slice(p, b0, p.B - b0 < step ? p.B - b0 : step), counter, stream, device);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 // Verifications of the no-allocation entry point, one at a time per device: they share that
@@ -316,7 +353,7 @@ int verify_fast(const Problem& p, hipStream_t stream, int device, bool noalloc, 
     int st = run_kernel(Kernel::Fast, p, stream, device);
     if (st != LTX3DROPE_OK) return st;
     if (launch_zero_u32(counter, stream) != hipSuccess) return LTX3DROPE_E_HIP;
-    if (launch_verify(p, counter, stream, device) != hipSuccess || hipGetLastError() != hipSuccess)
+    if (run_verify(p, counter, stream, device) != hipSuccess || hipGetLastError() != hipSuccess)
         return LTX3DROPE_E_HIP;
     unsigned host_count = 0;
     if (hipMemcpyAsync(&host_count, counter, sizeof(unsigned), hipMemcpyDeviceToHost, stream) != hipSuccess ||
@@ -909,7 +946,7 @@ const char* ltx3drope_reason_string(int reason) {
         case LTX3DROPE_REASON_TABLE_DEVICE: return "tables live on another device";
         case LTX3DROPE_REASON_ALIGN: return "pointers must be aligned to one (even, odd) pair";
         case LTX3DROPE_REASON_OVERLAP: return "outputs must not overlap the inputs or each other";
-        case LTX3DROPE_REASON_TOO_LARGE: return "tensors must have fewer than 2^32 elements";
+        case LTX3DROPE_REASON_TOO_LARGE: return "a batch element must have fewer than 2^32 elements";
         case LTX3DROPE_REASON_NOT_DEVICE_PTR: return "pointer is not device memory";
         case LTX3DROPE_REASON_HOST_MODE: return "host-table test mode: nothing is launched";
         case LTX3DROPE_REASON_EXTENT: return "a device allocation ends before the tensor does";

@@ -25,8 +25,9 @@ struct ltx3drope_tables {
 
 namespace ltx3drope {
 
-// Everything a kernel needs to know about one apply_qk call.  All sizes fit in
-// 32 bits because the precheck caps every tensor below 2^32 elements (pairs
+// Everything a kernel needs to know about one launch of an apply_qk call.  All
+// sizes fit in 32 bits: the precheck keeps a batch element below 2^32 elements
+// and a launch takes as many whole batch elements as stay below 2^32 (pairs
 // below 2^31, 16-byte vectors below 2^30).
 struct Problem {
     void* q_out;

@@ -669,3 +669,31 @@ def test_largest_supported_tensor():
     log("largest tensor: oracle comparison of every element")
     for x, out, name in ((dq, qo, "q"), (dk, ko, "k")):
         full_check(to_host(x, oracle.BF16), out, oracle.BF16, split, 10000.0, f"largest tensor {name}")
+
+
+def test_tensor_above_2_to_the_32_elements_runs_in_batch_slices():
+    """B = 2 batch elements of [16, 64, 1024] x 17 heads x head_dim 128 = 2,281,701,376 elements
+    each: 4,563,402,752 elements per tensor (8.5 GiB of bf16), above 2^32, so each kernel runs as
+    two launches of one batch element.  The gate verifies both slices, fast == plain over the
+    whole output, and every element of Q_out and K_out is compared with the oracle."""
+    shape, split = (2, 16, 64, 1024, 17, 128), (32, 48, 48)
+    log("above 2^32 elements: generating inputs on the device")
+    dq = workloads.generate_bf16_bits(shape, 201, DEV)
+    dk = workloads.generate_bf16_bits(shape, 202, DEV)
+    with rla.tables_build(16, 64, 1024, split) as tab:
+        assert rla.can_use(dq, dk, tab) == (True, "OK")
+        qo, ko = rla.apply_qk(dq, dk, tab)
+        torch.cuda.synchronize()
+        s = rla.stats()
+        assert rla.gate_state(0, rla.DTYPE_BF16, shape, split) == "TRUSTED"
+        assert s["gate_verifications"] == 1 and s["fast_launches"] == 2 and s["plain_launches"] == 0
+        rla.set_option(rla.OPT_PATH, 2)
+        pq, pk = rla.apply_qk(dq, dk, tab)
+        torch.cuda.synchronize()
+        assert rla.stats()["plain_launches"] == 2
+        assert torch.equal(qo.view(torch.int16), pq.view(torch.int16))
+        assert torch.equal(ko.view(torch.int16), pk.view(torch.int16))
+        del pq, pk
+    log("above 2^32 elements: oracle comparison of every element")
+    for x, out, name in ((dq, qo, "q"), (dk, ko, "k")):
+        full_check(to_host(x, oracle.BF16), out, oracle.BF16, split, 10000.0, f"above 2^32 elements {name}")

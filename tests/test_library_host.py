@@ -278,7 +278,7 @@ def case_for(rule, tab, tab_other_grid, tab_bad_split):
     if rule == "overlap":
         return (q + 64, ko, q, k, d, shp, tab)
     if rule == "too_large":
-        return (qo, ko, q, k, d, (1 << 12, 1, 1, 1 << 10, 1 << 8, 12), None)
+        return (qo, ko, q, k, d, (1, 1, 1, 1 << 10, 1 << 22, 12), None)
     return None
 
 
@@ -531,17 +531,21 @@ def test_binding_refuses_host_tensors_and_bad_patch_sizes_before_any_call():
     assert rla.stats()["rejected"] == 0  # nothing reached the library
 
 
-def test_size_limit_is_2_to_the_32_elements_per_tensor():
-    """The 3D RoPE takes tensors of up to 2^32 - 1 elements: just below passes the host rules,
-    2^32 is TOO_LARGE, and so is any single size of 2^31 or more."""
+def test_size_limit_is_2_to_the_32_elements_per_batch_element():
+    """A batch element of the 3D RoPE holds up to 2^32 - 1 elements: just below passes the host
+    rules, 2^32 is TOO_LARGE, and so is any single size of 2^31 or more.  A tensor of 2^32
+    elements or more made of smaller batch elements passes (it runs as several launches)."""
     split = (16, 16, 32)
     with rla.tables_build(1, 1, 1 << 20, split) as tab:
         base = 1 << 20
         args = (base + (1 << 40), base + (2 << 40), base, base + (4 << 40), _lib.DTYPE_BF16)
         assert call_can_use(*args, (1, 1, 1, 1 << 20, 63, 64), tab.handle) == (1, "OK")
         assert call_can_use(*args, (1, 1, 1, 1 << 20, 64, 64), tab.handle) == (0, "TOO_LARGE")
+        assert call_can_use(*args, (3, 1, 1, 1 << 20, 40, 64), tab.handle) == (1, "OK")  # 3 x 2.7 G elements
     with rla.tables_build(1, 1, 1, (2, 2, 2)) as tab:
         assert call_can_use(*args, (1 << 31, 1, 1, 1, 1, 6), tab.handle) == (0, "TOO_LARGE")
+        assert call_can_use(*args, ((1 << 31) - 1, 1, 1, 1, 1, 6), tab.handle) == (1, "OK")
+        assert call_can_use(*args, (1 << 30, 1, 1, 1, 1 << 20, 6), tab.handle) == (0, "TOO_LARGE")  # 2^52 in all
 
 
 def test_empty_calls_launch_nothing():
