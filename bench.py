@@ -46,7 +46,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 CSRC = os.path.join(ROOT, "rope_ltx3drope_amd", "csrc")
 # each timed kernel: its source file and the local headers it includes
 KERNEL_SOURCES = {
-    "rope_fast": ("kernels.hip", "stream_store.h", "internal.h", "fastdiv.h"),
+    "rope_fast": ("kernels.hip", "pair_math.h", "stream_store.h", "internal.h", "fastdiv.h"),
     "neox_fast": ("neox.hip", "stream_store.h", "internal.h"),
     "patch_lds": ("patchify.hip", "stream_store.h", "internal.h", "fastdiv.h"),
     "unpatch_lds": ("patchify.hip", "stream_store.h", "internal.h", "fastdiv.h"),

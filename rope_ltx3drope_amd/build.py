@@ -34,6 +34,7 @@ DEVICE = [
 ]
 SOURCES = [  # (file, language, extra flags)
     ("kernels.hip", "hip", DEVICE),
+    ("plain.hip", "hip", DEVICE),
     ("neox.hip", "hip", DEVICE),
     ("patchify.hip", "hip", DEVICE),
     ("dit_freqs.hip", "hip", DEVICE),

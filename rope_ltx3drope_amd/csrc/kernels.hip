@@ -15,17 +15,8 @@
 // and the w table for the rest; the table row is the token's t, h or w
 // coordinate, with token n = (t*H + h)*W + w in each batch element.
 //
-// Two kernels compute it:
-//  * rope_plain: one wavefront per (token, head) row of Q or of K, written
-//    from the eager definition: the row's token (t, h, w) is peeled from its
-//    place in the contiguous [B, T, H, W, heads, head_dim] layout; the lanes
-//    spread over the row's pairs, each finding its chunk (time, height, width)
-//    by walking the chunk widths, and rotating its pair with the table row of
-//    that axis's coordinate; scalar loads and stores, integer
-//    round-to-nearest-even.  It is the reference path of
-//    the bit-exact gate and the fallback for shapes the fast kernel does not
-//    cover.  With VERIFY it recomputes the result and counts pairs whose bits
-//    differ from what the outputs already hold.
+// Two kernels compute it: rope_plain (plain.hip), the gate's reference path and
+// the fallback, and this file's fast kernel:
 //  * rope_fast: a one-shot grid in which each thread owns one 16-byte vector
 //    (8 bf16 or 4 fp32 values, i.e. 4 or 2 pairs): the first half of the grid
 //    covers Q, the second half K.  When a token's heads*head_dim row is a whole
@@ -42,11 +33,11 @@
 //    LDS-staged tables and several vectors per lane.
 #include <hip/hip_runtime.h>
 
-#include <map>
 #include <mutex>
 
 #include "fastdiv.h"
 #include "internal.h"
+#include "pair_math.h"
 #include "stream_store.h"
 
 #pragma clang fp contract(off)
@@ -55,120 +46,8 @@ namespace ltx3drope {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kFastBlock = 64;             // one wavefront per workgroup
-constexpr int kPlainBlock = 256;
-
-// The pair (e, o) turned by the angle whose cosine and sine are (c, s): four
-// products, each rounded to fp32, then one rounded difference (even result)
-// and one rounded sum (odd result); nothing is fused.
-__device__ __forceinline__ void rotate(float e, float o, float c, float s, float& ye, float& yo) {
-    const float m0 = __fmul_rn(e, c), m1 = __fmul_rn(o, s);
-    const float m2 = __fmul_rn(e, s), m3 = __fmul_rn(o, c);
-    ye = __fsub_rn(m0, m1);
-    yo = __fadd_rn(m2, m3);
-}
-
-// bf16 <-> fp32.  A 32-bit word holds one pair: the even element in the low half.
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Integer round-to-nearest-even (plain path): add 0x7fff plus the lowest kept bit, keep the top half.
-__device__ __forceinline__ uint32_t bf16_rne_int(float y) {
-    const uint32_t u = __float_as_uint(y);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-// fp32 bits with any NaN replaced by the canonical quiet NaN.
-__device__ __forceinline__ uint32_t f32_canon(float y) { return y != y ? 0x7fc00000u : __float_as_uint(y); }
-
-// Hardware conversion of two floats to a packed bf16 pair (round to nearest
-// even), then any NaN half replaced by the canonical quiet NaN 0x7FC0.
-__device__ __forceinline__ uint32_t bf16_pack_hw(float lo, float hi) {
-    const f32x2 v = {lo, hi};
-    const bf16x2 r = __builtin_convertvector(v, bf16x2);
-    uint32_t w = __builtin_bit_cast(uint32_t, r);
-    if (lo != lo) w = (w & 0xffff0000u) | 0x7fc0u;
-    if (hi != hi) w = (w & 0x0000ffffu) | 0x7fc00000u;
-    return w;
-}
-
-// ---------------------------------------------------------------------------
-// plain kernel: one (token, head) row per wavefront
-// ---------------------------------------------------------------------------
-
-struct PlainArgs {
-    const void* src[2];  // Q, K
-    void* dst[2];        // Q_out, K_out
-    const float2* tab;   // packed (cos, sin) pairs: the t section, then h, then w
-    unsigned* mismatches;
-    uint32_t rows;              // (token, head) rows per tensor, B*T*H*W*heads; the grid covers both tensors
-    uint32_t heads, half_dim;   // heads per token, pairs per head row (head_dim / 2)
-    uint32_t T, H, W;           // the tensor's grid
-    uint32_t origin[3];         // coordinate of the tensor's first frame / row / column in the tables' grid
-    uint32_t width[3];          // pairs of the t, h and w chunks of a head row
-    uint32_t section[3];        // first pair of the t, h and w sections of the packed tables
-};
-
-template <bool BF16, bool VERIFY>
-__global__ void __launch_bounds__(kPlainBlock) rope_plain(PlainArgs a) {
-    constexpr uint32_t kWaves = kPlainBlock / 64;
-    uint32_t bad = 0;
-    const uint32_t lane = threadIdx.x % 64;
-    // 2 * rows < 2^32 (a tensor holds fewer than 2^32 elements, a row at least 2); the index is
-    // 64-bit so that adding the grid's stride cannot wrap
-    const uint64_t items = 2ull * a.rows;
-    const uint64_t stride = uint64_t(gridDim.x) * kWaves;
-    for (uint64_t item = uint64_t(blockIdx.x) * kWaves + threadIdx.x / 64; item < items; item += stride) {
-        const uint32_t x = item < a.rows ? 0 : 1;  // 0: Q, 1: K
-        const uint32_t row = static_cast<uint32_t>(item - x * uint64_t(a.rows));
-        // row = ((((b*T + t)*H + h)*W + w)*heads + head: peel the layout from the innermost axis out
-        uint32_t rest = row / a.heads;
-        uint32_t coord[3];
-        coord[2] = rest % a.W;
-        rest /= a.W;
-        coord[1] = rest % a.H;
-        rest /= a.H;
-        coord[0] = rest % a.T;
-        const uint32_t first = row * a.half_dim;  // the row's first (even, odd) pair; < 2^31
-        for (uint32_t i = lane; i < a.half_dim; i += 64) {
-            // the chunk that holds pair i of the row: walk the t, h and w widths
-            int axis = 0;
-            uint32_t j = i;
-            while (axis < 2 && j >= a.width[axis]) j -= a.width[axis++];
-            const float2 cs = a.tab[a.section[axis] + (coord[axis] + a.origin[axis]) * a.width[axis] + j];
-            const uint32_t pair = first + i;
-            float ye, yo;
-            if constexpr (BF16) {
-                const uint32_t in = static_cast<const uint32_t*>(a.src[x])[pair];
-                rotate(bf16_lo(in), bf16_hi(in), cs.x, cs.y, ye, yo);
-                const uint32_t out = bf16_rne_int(ye) | (bf16_rne_int(yo) << 16);
-                uint32_t* dst = static_cast<uint32_t*>(a.dst[x]) + pair;
-                if constexpr (VERIFY) {
-                    bad += *dst != out ? 1u : 0u;
-                } else {
-                    *dst = out;
-                }
-            } else {
-                const float2 in = static_cast<const float2*>(a.src[x])[pair];
-                rotate(in.x, in.y, cs.x, cs.y, ye, yo);
-                const uint2 out = make_uint2(f32_canon(ye), f32_canon(yo));
-                uint2* dst = static_cast<uint2*>(a.dst[x]) + pair;
-                if constexpr (VERIFY) {
-                    const uint2 have = *dst;
-                    bad += (have.x != out.x || have.y != out.y) ? 1u : 0u;
-                } else {
-                    *dst = out;
-                }
-            }
-        }
-    }
-    if constexpr (VERIFY) {
-        if (bad != 0) atomicAdd(a.mismatches, bad);
-    }
-}
 
 // ---------------------------------------------------------------------------
 // fast kernel: one 16-byte vector of Q and of K per thread, one-shot grid
@@ -386,63 +265,7 @@ __global__ void __launch_bounds__(kFastBlock) copy16(u32x4* __restrict__ dst, co
 // launch geometry
 // ---------------------------------------------------------------------------
 
-std::mutex g_geo_mu;
-std::map<int, int> g_cu_count;
-
-int cu_count(int device) {
-    std::lock_guard<std::mutex> lock(g_geo_mu);
-    auto it = g_cu_count.find(device);
-    if (it != g_cu_count.end()) return it->second;
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0) {
-        (void)hipGetLastError();
-        n = 256;
-    }
-    g_cu_count[device] = n;
-    return n;
-}
-
 uint32_t elem_size(const Problem& p) { return p.dtype == LTX3DROPE_DTYPE_F32 ? 4u : 2u; }
-
-PlainArgs plain_args(const Problem& p, unsigned* mismatches) {
-    PlainArgs a;
-    a.src[0] = p.q;
-    a.src[1] = p.k;
-    a.dst[0] = p.q_out;
-    a.dst[1] = p.k_out;
-    a.tab = reinterpret_cast<const float2*>(p.tab);
-    a.mismatches = mismatches;
-    a.rows = p.B * p.T * p.H * p.W * p.heads;  // < 2^31 (fewer than 2^32 elements, head_dim >= 2)
-    a.heads = p.heads;
-    a.half_dim = p.D / 2;
-    a.T = p.T;
-    a.H = p.H;
-    a.W = p.W;
-    a.origin[0] = p.t_off;
-    a.origin[1] = p.h_off;
-    a.origin[2] = p.w_off;
-    a.width[0] = p.PT;
-    a.width[1] = p.PH;
-    a.width[2] = p.PW;
-    a.section[0] = 0;
-    a.section[1] = p.tabT * p.PT;
-    a.section[2] = p.tabT * p.PT + p.tabH * p.PH;
-    return a;
-}
-
-template <bool VERIFY>
-hipError_t launch_plain_impl(const Problem& p, unsigned* mismatches, hipStream_t stream, int device) {
-    const PlainArgs a = plain_args(p, mismatches);
-    const uint64_t want = (2ull * a.rows + kPlainBlock / 64 - 1) / (kPlainBlock / 64);  // one row per wavefront
-    const uint64_t cap = static_cast<uint64_t>(cu_count(device)) * 32u;
-    const uint32_t blocks = static_cast<uint32_t>(want < cap ? want : cap);
-    if (blocks == 0) return hipSuccess;
-    if (p.dtype == LTX3DROPE_DTYPE_BF16)
-        hipLaunchKernelGGL((rope_plain<true, VERIFY>), dim3(blocks), dim3(kPlainBlock), 0, stream, a);
-    else
-        hipLaunchKernelGGL((rope_plain<false, VERIFY>), dim3(blocks), dim3(kPlainBlock), 0, stream, a);
-    return hipGetLastError();
-}
 
 }  // namespace
 
@@ -547,14 +370,6 @@ hipError_t launch_fast(const Problem& p, hipStream_t stream, int device) {
     const int dec = wave_token ? kDecodeWave : a.HV >= 32 ? kDecodeSpan : kDecodeLane;
     if (aligned) return launch_fast_tab<kTabAligned>(a, bf16, dec, blocks, stream);
     return launch_fast_tab<kTabPair>(a, bf16, dec, blocks, stream);
-}
-
-hipError_t launch_plain(const Problem& p, hipStream_t stream, int device) {
-    return launch_plain_impl<false>(p, nullptr, stream, device);
-}
-
-hipError_t launch_verify(const Problem& p, unsigned* mismatches, hipStream_t stream, int device) {
-    return launch_plain_impl<true>(p, mismatches, stream, device);
 }
 
 hipError_t launch_zero_u32(unsigned* ptr, hipStream_t stream) {
