@@ -343,6 +343,7 @@ def main():
         "timed_region_device_allocations": new_segments,
         "gpu_settle_ms": round(settle_ms, 1),
         "copy_ceiling_GBps": None if copy_gbs is None else round(copy_gbs, 1),
+        "pct_of_copy_ceiling": None if copy_gbs is None else round(100.0 * achieved / copy_gbs, 2),
         "parity": parity,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -458,6 +459,7 @@ def main_cycle(args):
                         "timed_misses": st["cache_misses"] - warm["cache_misses"],
                         "timed_hits": st["cache_hits"] - warm["cache_hits"]},
         "copy_ceiling_GBps": round(copy_gbs, 1),
+        "pct_of_copy_ceiling": round(100.0 * achieved / copy_gbs, 2),
         "parity": parity,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
@@ -543,6 +545,7 @@ def main_neox(args):
         "timed_region_device_allocations": new_segments,
         "gpu_settle_ms": round(settle_ms, 1),
         "copy_ceiling_GBps": round(copy_gbs, 1),
+        "pct_of_copy_ceiling": round(100.0 * alg / kavg / 1e9 / copy_gbs, 2),
         "parity": parity,
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4),
@@ -690,6 +693,7 @@ def main_patch(args):
         "timed_region_device_allocations": new_segments,
         "gpu_settle_ms": round(settle_ms, 1),
         "copy_ceiling_GBps": round(copy_gbs, 1),
+        "pct_of_copy_ceiling": round(100.0 * alg / kavg / 1e9 / copy_gbs, 2),
         "parity": parity,
         "roofline": {"bound": "hbm", "achieved": round(alg / kavg / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, kernel)},
