@@ -190,7 +190,8 @@ int ltx3drope_can_use(const void* q_out, const void* k_out, const void* q, const
  * call verified; equal -> the fast path is trusted, unequal -> permanent
  * fallback to the plain path for that configuration).  The gate's
  * configuration key is (device, dtype, B, T, H, W, heads, head_dim, dim_t,
- * dim_h, dim_w).  The comparison is of raw bits: both kernels write a NaN
+ * dim_h, dim_w, the tables' T, H, W and the shard offsets): each shard
+ * placement is verified on its own first call.  The comparison is of raw bits: both kernels write a NaN
  * result as the canonical quiet NaN (0x7FC00000 fp32, 0x7FC0 bf16).  On a
  * stream under graph capture an unverified configuration runs the plain
  * kernel and stays unverified (the check cannot wait for its count there).
@@ -351,7 +352,8 @@ int ltx3drope_unpatchify(void* x, const void* y, int elem_bytes, int64_t B, int6
 int ltx3drope_dit_freq_grid(double theta, int64_t dim, int64_t num_rope_elems, int double_precision, float* out,
                             void* stream, int64_t* count);
 
-/* Gate state of one configuration key (LTX3DROPE_GATE_*), or a negative status. */
+/* Gate state of one unsharded configuration (tables built for the tensor's own grid, no offsets):
+ * LTX3DROPE_GATE_*, or a negative status. */
 int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W,
                          int64_t heads, int64_t head_dim, int64_t dim_t, int64_t dim_h, int64_t dim_w);
 

@@ -66,7 +66,10 @@ Stats& stats() {
 
 // ---- gate ------------------------------------------------------------------
 
-using GateKey = std::tuple<int, int, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t>;
+// (device, dtype, B, T, H, W, heads, head_dim, dim_t, dim_h, dim_w, the tables' T, H, W, and the
+// tensor's t, h, w offsets in them): a shard placement is a configuration of its own.
+using GateKey = std::tuple<int, int, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t,
+                           int64_t, int64_t, int64_t, int64_t, int64_t, int64_t>;
 
 struct Gate {
     std::mutex mu;
@@ -411,7 +414,8 @@ int apply_impl(void* q_out, void* k_out, const void* q, const void* k, int dtype
 
     const int64_t gate_mode = opts().gate.load();
     if (gate_mode == 0) return run_kernel(Kernel::Fast, p, stream, device);
-    const GateKey key{device, dtype, B, T, H, W, heads, head_dim, tables->dim_t, tables->dim_h, tables->dim_w};
+    const GateKey key{device, dtype, B, T, H, W, heads, head_dim, tables->dim_t, tables->dim_h, tables->dim_w,
+                      tables->T, tables->H, tables->W, pl.t0, pl.h0, pl.w0};
     const int state = gate_get(key);
     if (state == LTX3DROPE_GATE_DISABLED) return run_kernel(Kernel::Plain, p, stream, device);
     const bool inplace = q_out == q || k_out == k;
@@ -837,7 +841,8 @@ int ltx3drope_dit_freq_grid(double theta, int64_t dim, int64_t num_rope_elems, i
 
 int ltx3drope_gate_state(int device, int dtype, int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads,
                          int64_t head_dim, int64_t dim_t, int64_t dim_h, int64_t dim_w) {
-    return gate_get(GateKey{device, dtype, B, T, H, W, heads, head_dim, dim_t, dim_h, dim_w});
+    // the unsharded configuration: tables built for the tensor's own grid, no offsets
+    return gate_get(GateKey{device, dtype, B, T, H, W, heads, head_dim, dim_t, dim_h, dim_w, T, H, W, 0, 0, 0});
 }
 
 int ltx3drope_gate_reset(void) {

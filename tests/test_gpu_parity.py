@@ -697,3 +697,22 @@ def test_tensor_above_2_to_the_32_elements_runs_in_batch_slices():
     log("above 2^32 elements: oracle comparison of every element")
     for x, out, name in ((dq, qo, "q"), (dk, ko, "k")):
         full_check(to_host(x, oracle.BF16), out, oracle.BF16, split, 10000.0, f"above 2^32 elements {name}")
+
+
+def test_each_shard_placement_is_verified_on_its_first_call():
+    """The gate's key holds the tables' grid and the shard's offsets: a slab of a larger grid is
+    verified on its own first call, a repeated placement is not verified again, and every
+    output equals the oracle."""
+    grid, shape, split = (6, 8, 9), (1, 2, 3, 4, 8, 64), (16, 24, 24)
+    q, k = workloads.generate_custom(shape, oracle.BF16, seed=77)
+    dq, dk = to_dev(q, oracle.BF16), to_dev(k, oracle.BF16)
+    placements = [(0, 0, 0), (3, 2, 5), (3, 2, 5), (1, 4, 2)]
+    with rla.tables_build(*grid, split) as tab:
+        for offsets in placements:
+            qo, ko = rla.apply_qk(dq, dk, tab, offsets=offsets)
+            torch.cuda.synchronize()
+            want_q, want_k = oracle.rope3d_qk(q, k, oracle.BF16, split, offsets=offsets, grid=grid)
+            assert_bitexact(to_host(qo, oracle.BF16), want_q, oracle.BF16, f"q at {offsets}")
+            assert_bitexact(to_host(ko, oracle.BF16), want_k, oracle.BF16, f"k at {offsets}")
+    s = rla.stats()
+    assert s["gate_verifications"] == 3 and s["gate_trusted"] == 3 and s["fast_launches"] == 4
