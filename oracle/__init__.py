@@ -23,6 +23,7 @@ from .rope import (  # noqa: F401
     apply_rope_tokens,
     axis_tables,
     bf16_bits_to_f32,
+    f32_canonical_nan,
     f32_to_bf16_bits,
     from_f32,
     grid_tables,

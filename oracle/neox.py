@@ -19,6 +19,9 @@ products and the sum are computed in fp32 and rounded once to q's dtype (for
 bf16, round to nearest even; for fp32, the fp32 rounding itself).  The cache
 may be fp32 or bf16; the gathered values are converted to q's dtype first.
 
+A NaN result is written as the canonical quiet NaN (0x7FC00000 in fp32, 0x7FC0
+in bf16), as in oracle.rope: the page says nothing about NaN payloads.
+
 Layout: q [tokens, q_heads, D], k [tokens, k_heads, D] (the head counts may
 differ), positions [tokens] integers in [0, max_position), cache
 [max_position, D] with the cos half first.  bf16 arrays are uint16 bit
@@ -28,7 +31,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .rope import BF16, F32, f32_to_bf16_bits, to_f32
+from .rope import BF16, F32, f32_canonical_nan, f32_to_bf16_bits, to_f32
 
 
 def round_to(x32: np.ndarray, dtype: str) -> np.ndarray:
@@ -63,7 +66,7 @@ def neox_rope(x: np.ndarray, dtype: str, positions: np.ndarray, cache: np.ndarra
         a = round_to(np.multiply(xf, cos, dtype=f), dtype)                # q * cos
         b = round_to(np.multiply(rotate_half(xf), sin, dtype=f), dtype)   # rotate_half(q) * sin
         y = round_to(np.add(a, b, dtype=f), dtype)                        # sum
-    return f32_to_bf16_bits(y) if dtype == BF16 else y
+    return f32_to_bf16_bits(y) if dtype == BF16 else f32_canonical_nan(y)
 
 
 def neox_rope_qk(q, k, dtype, positions, cache, cache_dtype):

@@ -23,7 +23,8 @@
 //  * neox_plain: one (i, i + D/2) element pair per thread, scalar accesses,
 //    integer round-to-nearest-even; any even head_dim, any 2-element alignment.
 // A position outside [0, max_position) is never dereferenced: the token's
-// outputs become NaN and the (token, tensor) is counted in `errors`.
+// outputs become NaN and the (token, tensor) is counted in `errors`.  Every NaN
+// output is the canonical quiet NaN (0x7FC00000 fp32, 0x7FC0 bf16).
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -53,6 +54,17 @@ __device__ __forceinline__ uint32_t rne_int(float y) {
     const uint32_t u = __float_as_uint(y);
     if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// fp32 bits with any NaN replaced by the canonical quiet NaN.
+__device__ __forceinline__ uint32_t canon_f32(float y) { return y != y ? 0x7fc00000u : __float_as_uint(y); }
+
+// Two fp32 results packed to bf16 (hardware conversion), any NaN written as the canonical 0x7FC0.
+__device__ __forceinline__ uint32_t pack_out(float lo, float hi) {
+    uint32_t w = pack_hw(lo, hi);
+    if (lo != lo) w = (w & 0xffff0000u) | 0x7fc0u;
+    if (hi != hi) w = (w & 0x0000ffffu) | 0x7fc00000u;
+    return w;
 }
 
 // Rounds two fp32 values to bf16 and back (hardware conversion).
@@ -180,16 +192,16 @@ __global__ void __launch_bounds__(kBlock) neox_fast(NeoxArgs a) {
                 round2_bf16(b1[0], b1[1]);
                 round2_bf16(a2[0], a2[1]);
                 round2_bf16(b2[0], b2[1]);
-                y1[w] = pack_hw(__fadd_rn(a1[0], b1[0]), __fadd_rn(a1[1], b1[1]));
-                y2[w] = pack_hw(__fadd_rn(a2[0], b2[0]), __fadd_rn(a2[1], b2[1]));
+                y1[w] = pack_out(__fadd_rn(a1[0], b1[0]), __fadd_rn(a1[1], b1[1]));
+                y2[w] = pack_out(__fadd_rn(a2[0], b2[0]), __fadd_rn(a2[1], b2[1]));
             }
         } else {
 #pragma unroll
             for (int j = 0; j < E; ++j) {
                 const float e1 = __uint_as_float(x1[j]);
                 const float e2 = __uint_as_float(x2[j]);
-                y1[j] = __float_as_uint(__fadd_rn(__fmul_rn(e1, c[j]), __fmul_rn(-e2, s[j])));
-                y2[j] = __float_as_uint(__fadd_rn(__fmul_rn(e2, c[j]), __fmul_rn(e1, s[j])));
+                y1[j] = canon_f32(__fadd_rn(__fmul_rn(e1, c[j]), __fmul_rn(-e2, s[j])));
+                y2[j] = canon_f32(__fadd_rn(__fmul_rn(e2, c[j]), __fmul_rn(e1, s[j])));
             }
         }
         stream_store16(y1, dst_tok, token_bytes, in_tok1);
@@ -253,8 +265,8 @@ __global__ void __launch_bounds__(256) neox_plain(NeoxArgs a) {
             const float* x = static_cast<const float*>(second ? a.k : a.q);
             float* d = static_cast<float*>(second ? a.k_out : a.q_out);
             const float e1 = x[e1i], e2 = x[e2i];
-            d[e1i] = __fadd_rn(__fmul_rn(e1, c), __fmul_rn(-e2, s));
-            d[e2i] = __fadd_rn(__fmul_rn(e2, c), __fmul_rn(e1, s));
+            d[e1i] = __uint_as_float(canon_f32(__fadd_rn(__fmul_rn(e1, c), __fmul_rn(-e2, s))));
+            d[e2i] = __uint_as_float(canon_f32(__fadd_rn(__fmul_rn(e2, c), __fmul_rn(e1, s))));
         }
     }
 }

@@ -46,12 +46,10 @@ def to_host(t, dtype):
 
 
 def assert_bitexact(got, want, dtype, what):
+    """Raw bits (NaN outputs are the canonical quiet NaN on both sides)."""
     g = got.view(np.uint32 if dtype == oracle.F32 else np.uint16)
     w = want.view(np.uint32 if dtype == oracle.F32 else np.uint16)
     neq = g != w
-    if neq.any():
-        both_nan = np.isnan(oracle.to_f32(got, dtype)) & np.isnan(oracle.to_f32(want, dtype))
-        neq &= ~both_nan
     n = int(neq.sum())
     assert n == 0, f"{what}: {n} mismatching elements, first at {np.argwhere(neq)[:3].tolist()}"
 
@@ -127,8 +125,9 @@ def test_out_of_range_positions_are_flagged_not_read():
         good[[3, 10, 11]] = False
         want_q = nx.neox_rope(q[good], w.dtype, pos[good], cache, w.cache_dtype)
         assert_bitexact(gq[good], want_q, w.dtype, "q on valid tokens")
-        assert np.isnan(oracle.to_f32(gq[~good], w.dtype)).all()
-        assert np.isnan(oracle.to_f32(gk[~good], w.dtype)).all()
+        canon = np.uint32(0x7FC00000) if w.dtype == oracle.F32 else np.uint16(0x7FC0)
+        raw = (lambda a: a.view(np.uint32)) if w.dtype == oracle.F32 else (lambda a: a)
+        assert (raw(gq[~good]) == canon).all() and (raw(gk[~good]) == canon).all()
 
 
 def test_full_size_sampled_and_fast_equals_plain():
@@ -257,3 +256,25 @@ def test_tensors_of_more_than_2_to_the_31_elements():
         want = nx.neox_rope(to_host(x[idx], oracle.BF16), oracle.BF16, pos, cache, oracle.BF16)
         assert_bitexact(to_host(out[idx], oracle.BF16), want, oracle.BF16, "sampled tokens")
     assert rla.neox_position_errors(0) == 0
+
+
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.F32])
+@pytest.mark.parametrize("path", [0, 2], ids=["fast", "plain"])
+def test_special_values_raw_bits(dtype, path):
+    """NaNs of several signs and payloads, infinities, zeros, huge and tiny values in Q and K: every
+    output equals the oracle's raw bits, NaN results being the canonical quiet NaN."""
+    w = workloads.NeoxWorkload("sv", dtype, 40, 4, 2, 64, 64, oracle.F32, "random", 91)
+    q, k, pos, cache = workloads.generate_neox(w)
+    rng = np.random.Generator(np.random.PCG64(92))
+    if dtype == oracle.F32:
+        special = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF812345, 0x7F800000, 0xFF800000, 0x80000000,
+                            0x00000001, 0x7F7FFFFF], np.uint32).view(np.float32)
+    else:
+        special = np.array([0x7FC0, 0xFFC0, 0x7F81, 0xFF92, 0x7F80, 0xFF80, 0x8000, 0x0001, 0x7F7F], np.uint16)
+    for x in (q, k):
+        flat = x.reshape(-1)
+        idx = rng.choice(flat.size, flat.size // 8, replace=False)
+        flat[idx] = special[rng.integers(0, len(special), idx.size)]
+    _, gq, gk = run(w, path, q, k, pos, cache)
+    assert_bitexact(gq, nx.neox_rope(q, dtype, pos, cache, oracle.F32), dtype, "q")
+    assert_bitexact(gk, nx.neox_rope(k, dtype, pos, cache, oracle.F32), dtype, "k")

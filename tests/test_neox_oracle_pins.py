@@ -117,6 +117,19 @@ def pin_error_bound(dtype=oracle.BF16, seed=6):
     assert np.all(np.abs(got - exact) <= mag * 2 * u + np.abs(exact) * 2 * u + 1e-30)
 
 
+def pin_nan_canonical():
+    """A NaN result is the canonical quiet NaN whatever the sign and payload of the NaN input."""
+    for dtype, nans, canon in ((oracle.F32, np.array([0xFFC00000, 0x7F800001, 0xFF812345], np.uint32).view(np.float32),
+                                0x7FC00000),
+                               (oracle.BF16, np.array([0xFFC0, 0x7F81, 0xFF92], np.uint16), 0x7FC0)):
+        q, pos, cache = _inputs(tokens=4, heads=2, D=8, dtype=dtype, seed=12)
+        q.reshape(-1)[[0, 5, 9]] = nans
+        out = nx.neox_rope(q, dtype, pos, cache, oracle.F32)
+        raw = out.view(np.uint32) if dtype == oracle.F32 else out
+        nan = np.isnan(oracle.to_f32(out, dtype))
+        assert nan.sum() >= 3 and np.all(raw[nan] == canon)
+
+
 ALL_PINS = [
     ("fp32_vs_3d", pin_fp32_equals_interleaved_3d_oracle),
     ("torch_bf16_f32cache", lambda: pin_torch_expression(oracle.BF16, oracle.F32)),
@@ -124,6 +137,7 @@ ALL_PINS = [
     ("torch_f32", lambda: pin_torch_expression(oracle.F32, oracle.F32)),
     ("closed_forms", pin_identity_and_unit_vectors),
     ("bound_bf16", pin_error_bound),
+    ("nan_canonical", pin_nan_canonical),
 ]
 
 
@@ -181,12 +195,24 @@ def _neox_cos_sin_swapped(x, dtype, positions, cache, cache_dtype):
     return nx.__dict__["_orig_neox_rope"](x, dtype, positions, sw, cache_dtype)
 
 
+def _neox_keeps_nan_payload(x, dtype, positions, cache, cache_dtype):
+    y = nx.__dict__["_orig_neox_rope"](x, dtype, positions, cache, cache_dtype)
+    if dtype != oracle.F32:
+        return y
+    xf = np.asarray(x, np.float32)
+    out = y.copy()
+    nan = np.isnan(out) & np.isnan(xf)
+    out[nan] = xf[nan]  # the input's NaN pattern instead of the canonical one
+    return out
+
+
 MUTATIONS = [
     ("rotate_half", _rh_wrong_sign),
     ("rotate_half", _rh_interleaved),
     ("round_to", _round_to_skip_bf16),
     ("neox_rope", _neox_positions_ignored),
     ("neox_rope", _neox_cos_sin_swapped),
+    ("neox_rope", _neox_keeps_nan_payload),
 ]
 
 
