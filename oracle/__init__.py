@@ -10,8 +10,9 @@ inverse frequencies, tables against an arbitrary-precision evaluation,
 unit-vector readback, identity at position 0, norm preservation, a +theta /
 -theta round trip, an error bound against the exact complex product, a
 brute-force per-element angle recomputation on tiny grids, the bf16 cast
-against torch's CPU cast and its closed-form properties.  Parity with
-sglang's own table bits is unpinned (no values are printed on the pages).
+against torch's CPU cast and its closed-form properties.  Every function
+here has such pins.  Bit identity with sglang's own tables cannot be
+checked: the pages print no table values.
 
 oracle.neox: the rotate-half RoPE with a gathered cos/sin cache (pins in
 tests/test_neox_oracle_pins.py).

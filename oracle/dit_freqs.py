@@ -23,8 +23,8 @@ to the working dtype, round to nearest even:
 * theta ** x is the correctly rounded power in the working dtype; for
   float32, theta (a Python float) is first rounded to float32, as torch does
   with a scalar base and a float32 exponent.  The bits of a device's own pow
-  routine are not printed anywhere, so parity with any particular pow
-  implementation beyond its error bound is unpinned.
+  routine are not printed anywhere, so bit identity with any particular pow
+  implementation cannot be checked beyond that routine's error bound.
 * p * pi uses pi rounded to the working dtype and is rounded once; the
   division by 2 is exact; the float64 recipe rounds once more to float32.
 

@@ -15,8 +15,8 @@ and 2, and "Key source snippets", the CUDA kernel snippet):
   does not print its formula; this is the textbook inverse-frequency RoPE
   that the builder replaced (_inv_freqs), with integer positions because the
   cache key carries no offset or scale.  Computed in float64 (Python's math
-  module) and rounded once to fp32.  Parity of this reading with sglang's own
-  table bits is unpinned: no table values are printed anywhere.
+  module) and rounded once to fp32.  Whether sglang's own tables hold the
+  same bits cannot be checked: no table values are printed anywhere.
 
 * The eager rotation.  The head dimension is cut into a time, a height and a
   width chunk of (dim_t, dim_h, dim_w) channels, in that order.  Each chunk

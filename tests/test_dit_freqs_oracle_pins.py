@@ -7,7 +7,7 @@
   libm within 1 ulp (equal almost always).
 * the whole grid: torch evaluating the page's expression on the CPU -- 0 ulp for the
   float64 recipe, at most 2 ulp for the float32 one, where torch's own float32 pow may
-  land one unit away from the correctly rounded power (parity unpinned below that bound);
+  land one unit away from the correctly rounded power;
   closed forms at both ends and the geometric ratio.
 * planted mistakes that these pins must catch.
 """
