@@ -315,6 +315,7 @@ def main():
     if not args.inplace:
         assert torch.equal(sets[last_in][0], q) and torch.equal(sets[last_in][1], k)
     copy_gbs = copy_ceiling(sets, stream)
+    other_copies = platform_copies(sets[0], stream)
     parity, cpu = cpu_leg_rope3d(w, gi, q_np, k_np, qo, ko, applied[last_in] if args.inplace else 0, args)
 
     traffic = measured_traffic(w.name)
@@ -344,6 +345,7 @@ def main():
         "gpu_settle_ms": round(settle_ms, 1),
         "copy_ceiling_GBps": None if copy_gbs is None else round(copy_gbs, 1),
         "pct_of_copy_ceiling": None if copy_gbs is None else round(100.0 * achieved / copy_gbs, 2),
+        "platform_copies_GBps": other_copies,
         "parity": parity,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -773,6 +775,34 @@ def copy_ceiling(sets, stream, reps_per_set: int = 10) -> float:
     c1.record(stream)
     torch.cuda.synchronize()
     return bytes_per_step / (c0.elapsed_time(c1) / reps / 1e3) / 1e9
+
+
+def platform_copies(tensors, stream, reps: int = 10) -> dict:
+    """GB/s of the platform's own device-to-device copies over the same tensors, beside the
+    library's copy kernel: hipMemcpyAsync (torch's copy_ of a contiguous tensor of the same dtype,
+    which HIP serves with its blit kernel) and torch's vectorized elementwise kernel (neg, one
+    read and one write per element).  Shows whether the copy kernel's rate is the chip's streaming
+    rate or an artefact of its own launch shape."""
+    import torch
+
+    dsts = [torch.empty_like(t) for t in tensors]
+    nbytes = sum(2 * t.numel() * t.element_size() for t in tensors)
+    out = {}
+    for name, fn in (("hipMemcpyAsync_d2d", lambda d, t: d.copy_(t)),
+                     ("torch_elementwise_neg", lambda d, t: torch.neg(t, out=d))):
+        for _ in range(3):
+            for d, t in zip(dsts, tensors):
+                fn(d, t)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(reps):
+            for d, t in zip(dsts, tensors):
+                fn(d, t)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = round(nbytes / (c0.elapsed_time(c1) / reps / 1e3) / 1e9, 1)
+    del dsts
+    return out
 
 
 def patch_workload_name(op: str, shape, p: int, elem_bytes: int) -> str:
