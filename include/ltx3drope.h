@@ -73,9 +73,11 @@ enum {
     LTX3DROPE_REASON_TABLE_DEVICE = 7,   /* the tables live on another device than the tensors */
     LTX3DROPE_REASON_ALIGN = 8,          /* a pointer is not aligned to one pair (2 elements) */
     LTX3DROPE_REASON_OVERLAP = 9,        /* an output overlaps an input or the other output */
-    LTX3DROPE_REASON_TOO_LARGE = 10,     /* a tensor of 2^32 elements or more */
+    LTX3DROPE_REASON_TOO_LARGE = 10,     /* a batch element of 2^32 elements or more, a size of 2^31 or more,
+                                            or more than 2^48 elements in all */
     LTX3DROPE_REASON_NOT_DEVICE_PTR = 11,/* a pointer is not device memory of the tables' device */
-    LTX3DROPE_REASON_HOST_MODE = 12,     /* the library is in host-table test mode (no launches) */
+    LTX3DROPE_REASON_HOST_MODE = 12,     /* host-table test mode: apply calls refused, nothing launched (a name
+                                            for that refusal; the precheck itself never returns it) */
     LTX3DROPE_REASON_EXTENT = 13         /* a pointer's device allocation ends before the tensor does */
 };
 
@@ -85,7 +87,9 @@ enum {
     LTX3DROPE_OPT_GATE = 2,        /* 0 off (trust fast), 1 verify the first call per key (default), 2 verify every call */
     LTX3DROPE_OPT_FORCE_GATE_MISMATCH = 3, /* 1: every verification reports a mismatch (tests the fallback) */
     LTX3DROPE_OPT_HOST_TABLES = 4, /* 1: tables are built in host memory and nothing touches HIP (CPU tests of the
-                                      cache and the precheck); apply_qk then refuses with REASON_HOST_MODE */
+                                      cache and the precheck); can_use still reports the precheck's verdict
+                                      (memory checks skipped), and every apply call with such tables returns
+                                      E_UNSUPPORTED without launching */
     LTX3DROPE_OPT_LOG = 5          /* 1: one stderr line per gate decision */
 };
 

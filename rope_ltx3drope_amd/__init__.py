@@ -62,6 +62,14 @@ def _check(status: int, what: str) -> None:
         raise Ltx3dRopeError(status, what)
 
 
+def _refused(status: int, reason: ctypes.c_int, what: str):
+    """The error for an apply call that the library refused: the precheck's reason, or, where the
+    precheck passes, the library's refusal of host-memory tables (host-table test mode)."""
+    if reason.value == 0:
+        return Ltx3dRopeUnsupported("HOST_MODE" if get_option(OPT_HOST_TABLES) else f"{what}: refused", status)
+    return Ltx3dRopeUnsupported(_lib.REASONS.get(reason.value, str(reason.value)), status)
+
+
 def _torch():
     import torch
 
@@ -244,7 +252,7 @@ def apply_qk(q, k, tabs: Tables, q_out=None, k_out=None, stream=None, offsets=No
             _lib.lib().ltx3drope_can_use(*args, tabs.handle, ctypes.byref(reason))
         else:
             _lib.lib().ltx3drope_can_use_shard(*args, ctypes.byref(sh), tabs.handle, ctypes.byref(reason))
-        raise Ltx3dRopeUnsupported(_lib.REASONS.get(reason.value, str(reason.value)), st)
+        raise _refused(st, reason, "apply_qk")
     _check(st, "apply_qk")
     return q_out, k_out
 
@@ -261,7 +269,7 @@ def apply_qk_noalloc(q, k, tabs: Tables, q_out, k_out, stream=None):
     if st in (_lib.E_UNSUPPORTED, _lib.E_TABLE_MISMATCH):
         reason = ctypes.c_int(0)
         _lib.lib().ltx3drope_can_use(*args, tabs.handle, ctypes.byref(reason))
-        raise Ltx3dRopeUnsupported(_lib.REASONS.get(reason.value, str(reason.value)), st)
+        raise _refused(st, reason, "apply_qk_noalloc")
     _check(st, "apply_qk_noalloc")
     return q_out, k_out
 

@@ -496,6 +496,28 @@ def test_precheck_on_device_pointers():
     assert rla.stats()["fast_launches"] == 0 and rla.stats()["plain_launches"] == 0
 
 
+def test_host_table_mode_refuses_apply_and_names_it():
+    """Tables built in host-table test mode pass the precheck (its memory checks are skipped), but no
+    apply entry point launches with them; the binding names that refusal HOST_MODE."""
+    shape, split = (1, 2, 3, 4, 2, 12), (4, 4, 4)
+    q = torch.zeros(shape, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros_like(q)
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    rla.set_option(rla.OPT_HOST_TABLES, 1)
+    try:
+        with rla.tables_build(2, 3, 4, split) as tab:
+            assert rla.can_use(q, k, tab) == (True, "OK")
+            for call in (lambda: rla.apply_qk(q, k, tab), lambda: rla.apply_qk_noalloc(q, k, tab, qo, ko)):
+                with pytest.raises(rla.Ltx3dRopeUnsupported) as ei:
+                    call()
+                assert ei.value.reason == "HOST_MODE" and ei.value.status == _lib.E_UNSUPPORTED
+    finally:
+        rla.set_option(rla.OPT_HOST_TABLES, 0)
+        rla.cache_clear()
+    s = rla.stats()
+    assert s["fast_launches"] == 0 and s["plain_launches"] == 0 and s["rejected"] == 2
+
+
 def test_side_stream_and_forward_pair():
     shape, split = (1, 4, 8, 8, 16, 128), (32, 48, 48)
     q, k = workloads.generate_custom(shape, oracle.BF16, seed=12)
