@@ -915,23 +915,41 @@ def cpu_leg_compare_all(x_np, got_np, dtype, split, base, threads: int):
 
 
 def cpu_leg_neox(w, q_np, k_np, pos_np, cache_np, qo, ko, args):
-    """Rotate-half RoPE: the oracle on 256 sampled tokens against the GPU outputs, then the timed
-    oracle on consecutive chunks.  Returns (parity, cpu_baseline or None)."""
+    """Rotate-half RoPE.  Parity: every element of the GPU outputs qo, ko against the oracle,
+    computed over blocks of consecutive tokens by a pool of threads; then, unless
+    --no-cpu-baseline, the oracle timed on one core over consecutive chunks.  Returns (parity,
+    cpu_baseline or None)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
-    import torch
 
     import oracle.neox as nx
-    import workloads
 
-    ids = workloads.sample_tokens(w.tokens, 256, seed=99)
-    idx = torch.from_numpy(ids).to(qo.device)
-    mism = 0
-    for x_np, out in ((q_np, qo), (k_np, ko)):
-        want = nx.neox_rope(x_np[ids], w.dtype, pos_np[ids], cache_np, w.cache_dtype)
-        got = out[idx].cpu()
-        got = got.view(torch.int16).numpy().view(np.uint16) if w.dtype == workloads.BF16 else got.numpy()
-        mism += int((got.view(want.dtype) != want).sum())
-    parity = {"sampled_tokens": int(len(ids)), "mismatching_elements": mism, "tolerance_ulp": 0}
+    threads = max(1, args.cpu_threads)
+    mism, first = 0, None
+    for name, x_np, out in (("q", q_np, qo), ("k", k_np, ko)):
+        got_np = _host_bits(out, w.itemsize)
+        view = (lambda a: a.view(np.uint32)) if got_np.dtype == np.float32 else (lambda a: a)
+        step = max(1, (1 << 23) // (x_np.shape[1] * x_np.shape[2]))
+
+        def block(t0, x_np=x_np, got_np=got_np, view=view, step=step, name=name):
+            t1 = min(w.tokens, t0 + step)
+            want = nx.neox_rope(np.ascontiguousarray(x_np[t0:t1]), w.dtype, pos_np[t0:t1], cache_np, w.cache_dtype)
+            neq = view(got_np[t0:t1]) != view(want)
+            n = int(neq.sum())
+            if not n:
+                return 0, None
+            i = tuple(int(v) for v in np.argwhere(neq)[0])
+            return n, {"tensor": name, "index": [t0 + i[0]] + list(i[1:]), "got": hex(int(view(got_np[t0:t1])[i])),
+                       "want": hex(int(view(want)[i]))}
+
+        with ThreadPoolExecutor(threads) as ex:
+            res = list(ex.map(block, range(0, w.tokens, step)))
+        mism += sum(n for n, _ in res)
+        first = first or next((f for n, f in res if n), None)
+    parity = {"compared_elements": int(q_np.size + k_np.size), "mismatching_elements": mism, "tolerance_ulp": 0}
+    if first:
+        parity["first_mismatch"] = first
     cpu = None if args.no_cpu_baseline else neox_cpu_baseline(w, q_np, k_np, pos_np, cache_np, args.cpu_seconds)
     return parity, cpu
 

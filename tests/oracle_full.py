@@ -1,6 +1,6 @@
-"""Whole-tensor comparison of a GPU result with the 3D RoPE oracle at full size.
+"""Whole-tensor comparison of a GPU result with the oracle at full size (3D RoPE and rotate-half RoPE).
 
-The oracle is applied one block of rows of one (batch, frame) at a time -- each block as a shard of
+For the 3D RoPE the oracle is applied one block of rows of one (batch, frame) at a time -- each block as a shard of
 the whole grid, with the whole grid's tables -- from a pool of threads (numpy releases the
 interpreter lock inside its array operations), and every element of the block is compared bit for
 bit with the same block of the GPU output.  Blocks hold at most about 8 M elements, which bounds
@@ -62,3 +62,32 @@ def compare_full(x_host: np.ndarray, got_host: np.ndarray, dtype: str, split, ba
     total = sum(n for n, _ in results)
     first = next((f for n, f in results if n), None)
     return total, first
+
+
+def compare_full_neox(x_host: np.ndarray, got_host: np.ndarray, dtype: str, positions: np.ndarray,
+                      cache: np.ndarray, cache_dtype: str, threads: int | None = None):
+    """(mismatching elements, first mismatch or None) of got_host against oracle.neox on x_host
+    ([tokens, heads, D]), every element, 0 ULP on raw bits.  The oracle runs over blocks of
+    consecutive tokens (at most about 8 M elements each, every token with its own position's
+    cache row) from a pool of threads."""
+    import oracle.neox as nx
+
+    tokens, heads, D = x_host.shape
+    assert got_host.shape == x_host.shape and got_host.dtype == x_host.dtype
+    step = max(1, BLOCK_ELEMS // (heads * D))
+
+    def block(t0):
+        t1 = min(tokens, t0 + step)
+        want = nx.neox_rope(np.ascontiguousarray(x_host[t0:t1]), dtype, positions[t0:t1], cache, cache_dtype)
+        got = got_host[t0:t1]
+        neq = bits(got) != bits(want)
+        n = int(neq.sum())
+        first = None
+        if n:
+            idx = tuple(int(v) for v in np.argwhere(neq)[0])
+            first = ((t0 + idx[0],) + idx[1:], hex(int(bits(got)[idx])), hex(int(bits(want)[idx])))
+        return n, first
+
+    with ThreadPoolExecutor(threads or pool_threads()) as ex:
+        results = list(ex.map(block, range(0, tokens, step)))
+    return sum(n for n, _ in results), next((f for n, f in results if n), None)

@@ -139,3 +139,36 @@ def test_cpu_leg_compares_every_element():
         raw[0, 0, 0, 0, 0, 0] ^= 2
         n, first = bench.cpu_leg_compare_all(q, bad, dtype, split, 10000.0, 3)
         assert n == 2 and first["index"] == [0, 0, 0, 0, 0, 0]
+
+
+def test_neox_cpu_leg_compares_every_element():
+    """The rotate-half bench line's parity pass over blocks of tokens: the oracle's own output
+    passes with every element counted, and a planted difference is found and located."""
+    import argparse
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import oracle.neox as nx
+    import workloads
+
+    args = argparse.Namespace(cpu_threads=3, no_cpu_baseline=True, cpu_seconds=0.0)
+    for key in ("n1", "n3"):
+        w = workloads.NEOX_WORKLOADS[key]
+        q, k, pos, cache = workloads.generate_neox(w)
+        wq = nx.neox_rope(q, w.dtype, pos, cache, w.cache_dtype)
+        wk = nx.neox_rope(k, w.dtype, pos, cache, w.cache_dtype)
+
+        def as_torch(a):
+            t = torch.from_numpy(a.view(np.int16) if w.dtype == oracle.BF16 else a.copy())
+            return t.view(torch.bfloat16) if w.dtype == oracle.BF16 else t
+
+        parity, cpu = bench.cpu_leg_neox(w, q, k, pos, cache, as_torch(wq), as_torch(wk), args)
+        assert cpu is None
+        assert parity["compared_elements"] == q.size + k.size and parity["mismatching_elements"] == 0
+        bad = wk.copy()
+        (bad.view(np.uint32) if w.dtype == oracle.F32 else bad)[w.tokens - 1, 1, 5] ^= 1
+        parity, _ = bench.cpu_leg_neox(w, q, k, pos, cache, as_torch(wq), as_torch(bad), args)
+        assert parity["mismatching_elements"] == 1
+        assert parity["first_mismatch"]["tensor"] == "k" and parity["first_mismatch"]["index"] == [w.tokens - 1, 1, 5]
