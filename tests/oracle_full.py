@@ -1,4 +1,5 @@
-"""Whole-tensor comparison of a GPU result with the oracle at full size (3D RoPE and rotate-half RoPE).
+"""Whole-tensor comparison of a GPU result with the oracle at full size (3D RoPE, rotate-half RoPE,
+patchify).
 
 For the 3D RoPE the oracle is applied one block of rows of one (batch, frame) at a time -- each block as a shard of
 the whole grid, with the whole grid's tables -- from a pool of threads (numpy releases the
@@ -91,3 +92,21 @@ def compare_full_neox(x_host: np.ndarray, got_host: np.ndarray, dtype: str, posi
     with ThreadPoolExecutor(threads or pool_threads()) as ex:
         results = list(ex.map(block, range(0, tokens, step)))
     return sum(n for n, _ in results), next((f for n, f in results if n), None)
+
+
+def compare_full_patchify(x_host: np.ndarray, y_host: np.ndarray, p: int, threads: int | None = None) -> int:
+    """Elements of the patchified y_host that differ from oracle.patchify applied to x_host, over
+    every (batch, channel, frame) plane, from a pool of threads."""
+    import oracle.patchify as pf
+
+    B, C, F, H, W = x_host.shape
+    assert y_host.shape == (B, C * p * p, F, H // p, W // p) and y_host.dtype == x_host.dtype
+
+    def plane(job):
+        b, c, f = job
+        want = pf.patchify(x_host[b:b + 1, c:c + 1, f:f + 1], p)[0, :, 0]
+        return int((y_host[b, c * p * p:(c + 1) * p * p, f] != want).sum())
+
+    jobs = [(b, c, f) for b in range(B) for c in range(C) for f in range(F)]
+    with ThreadPoolExecutor(threads or pool_threads()) as ex:
+        return sum(ex.map(plane, jobs))

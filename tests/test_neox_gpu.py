@@ -211,8 +211,8 @@ def test_random_configurations(seed):
 
 def test_more_tokens_than_the_fast_grid_holds_use_the_plain_kernel():
     """2^25 + 3 tokens of one head of 16 bf16 values: two 64-lane workgroups per token would need
-    2^32 work-items or more, so the call runs on the plain kernel; sampled tokens (the last
-    included) against the oracle.  Inputs are drawn on the device (workloads.generate_neox_device)."""
+    2^32 work-items or more, so the call runs on the plain kernel; every element against the
+    oracle.  Inputs are drawn on the device (workloads.generate_neox_device)."""
     tokens, D, maxp = (1 << 25) + 3, 16, 1000
     log("2^25 + 3 tokens: generating inputs on the device")
     dq, dk, dpos = workloads.generate_neox_device(tokens, 1, 1, D, maxp, 2024, DEV)
@@ -223,18 +223,18 @@ def test_more_tokens_than_the_fast_grid_holds_use_the_plain_kernel():
     s = rla.stats()
     assert s["plain_launches"] == 1 and s["fast_launches"] == 0
     assert rla.neox_position_errors(0) == 0
-    ids = np.unique(np.concatenate([workloads.sample_tokens(tokens, 2000, seed=5), [tokens - 2, tokens - 3]]))
-    idx = torch.from_numpy(ids).to(DEV)
-    pos = dpos[idx].cpu().numpy()
-    for x, out in ((dq, qo), (dk, ko)):
-        want = nx.neox_rope(to_host(x[idx], oracle.BF16), oracle.BF16, pos, cache, oracle.F32)
-        assert_bitexact(to_host(out[idx], oracle.BF16), want, oracle.BF16, "sampled tokens")
+    pos = dpos.cpu().numpy()
+    for name, x, out in (("q", dq, qo), ("k", dk, ko)):
+        log(f"2^25 + 3 tokens: comparing every element of {name} with the oracle")
+        n, first = compare_full_neox(to_host(x, oracle.BF16), to_host(out, oracle.BF16), oracle.BF16, pos, cache,
+                                     oracle.F32)
+        assert n == 0, f"{name}: {n} mismatching elements, first {first}"
 
 
 def test_tensors_of_more_than_2_to_the_31_elements():
     """2^23 tokens of one query and one KV head of head_dim 384 in bf16: 3,221,225,472 elements per
     tensor (between 2^31 and 2^32, 6.4 GB), drawn on the device.  The fast kernel against the plain
-    kernel over the whole output, and sampled tokens (the last included) against the oracle."""
+    kernel over the whole output, and every element against the oracle."""
     tokens, D, maxp = 1 << 23, 384, 4096
     log("2^23 tokens x 384: generating inputs on the device")
     dq, dk, dpos = workloads.generate_neox_device(tokens, 1, 1, D, maxp, 77, DEV)
@@ -250,12 +250,12 @@ def test_tensors_of_more_than_2_to_the_31_elements():
     assert torch.equal(fq.view(torch.int16), pq.view(torch.int16))
     assert torch.equal(fk.view(torch.int16), pk.view(torch.int16))
     del pq, pk
-    ids = workloads.sample_tokens(tokens, 1500, seed=8)
-    idx = torch.from_numpy(ids).to(DEV)
-    pos = dpos[idx].cpu().numpy()
-    for x, out in ((dq, fq), (dk, fk)):
-        want = nx.neox_rope(to_host(x[idx], oracle.BF16), oracle.BF16, pos, cache, oracle.BF16)
-        assert_bitexact(to_host(out[idx], oracle.BF16), want, oracle.BF16, "sampled tokens")
+    pos = dpos.cpu().numpy()
+    for name, x, out in (("q", dq, fq), ("k", dk, fk)):
+        log(f"2^23 tokens x 384: comparing every element of {name} with the oracle")
+        n, first = compare_full_neox(to_host(x, oracle.BF16), to_host(out, oracle.BF16), oracle.BF16, pos, cache,
+                                     oracle.BF16)
+        assert n == 0, f"{name}: {n} mismatching elements, first {first}"
     assert rla.neox_position_errors(0) == 0
 
 

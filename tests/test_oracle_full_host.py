@@ -62,3 +62,17 @@ def test_compare_full_neox_catches_positions_shifted_by_a_block():
     wrong = nx.neox_rope(q, w.dtype, np.roll(pos, 5), cache, w.cache_dtype)
     n, _ = oracle_full.compare_full_neox(q, wrong, w.dtype, pos, cache, w.cache_dtype, threads=2)
     assert n > 0
+
+
+def test_compare_full_patchify_planes_agree_with_the_whole_tensor():
+    import oracle.patchify as pf
+
+    x = workloads.generate_patch((2, 3, 4, 8, 12), 2, seed=3)
+    y = pf.patchify(x, 4)
+    assert oracle_full.compare_full_patchify(x, y, 4, threads=3) == 0
+    bad = y.copy()
+    bad[1, 2 * 16 + 5, 3, 1, 2] ^= 1
+    assert oracle_full.compare_full_patchify(x, bad, 4, threads=3) == 1
+    # the channel packing order matters: height and width offsets swapped must fail
+    swapped = x.reshape(2, 3, 4, 2, 4, 3, 4).transpose(0, 1, 4, 6, 2, 3, 5).reshape(2, 48, 4, 2, 3)
+    assert oracle_full.compare_full_patchify(x, np.ascontiguousarray(swapped), 4, threads=3) > 0
