@@ -253,8 +253,9 @@ typedef struct {
 } ltx3drope_shard_t;
 
 /* The precheck of a shard call: as ltx3drope_can_use, with the grid rule replaced by the shard's
-   containment rule and the in-place exception to the overlap rule.  Negative offsets or a non-zero
-   reserved field fail with REASON_TABLE_GRID. */
+   containment rule and the in-place exception to the overlap rule.  A malformed descriptor (a
+   negative offset, an inplace value other than 0 or 1, or a non-zero reserved field) fails with
+   REASON_TABLE_GRID before any other rule is looked at. */
 int ltx3drope_can_use_shard(const void* q_out, const void* k_out, const void* q, const void* k, int dtype,
                             int64_t B, int64_t T, int64_t H, int64_t W, int64_t heads, int64_t head_dim,
                             const ltx3drope_shard_t* shard, ltx3drope_tables_t tables, int* reason);
