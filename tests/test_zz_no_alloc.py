@@ -90,3 +90,59 @@ def test_noalloc_refuses_what_the_precheck_refuses():
         st = call("ltx3drope_apply_qk_noalloc", oracle.BF16, q, q.clone(), torch.empty_like(q), torch.empty_like(q),
                   tab)
     assert st == _lib.E_TABLE_MISMATCH
+
+
+def test_noalloc_verifications_from_threads_share_the_scratch_safely():
+    """Four host threads, each on its own stream, call the no-allocation entry point three times on
+    configurations of their own with every call verified: all verifications count in the one static
+    scratch counter, which the library hands to one verification at a time, so none may see
+    another's count (a stray count would disable the fast kernel) and every output equals the
+    oracle's."""
+    import threading
+
+    cases = [((1, 2, 4, 4, 8, 64), (16, 24, 24)), ((1, 3, 4, 6, 4, 96), (32, 32, 32)),
+             ((2, 2, 3, 5, 6, 64), (16, 16, 32)), ((1, 4, 2, 8, 8, 128), (32, 48, 48))]
+    inputs = [workloads.generate_custom(shape, oracle.BF16, seed=900 + i) for i, (shape, _) in enumerate(cases)]
+    dev_in = [(to_dev(q, oracle.BF16), to_dev(k, oracle.BF16)) for q, k in inputs]
+    streams = [torch.cuda.Stream() for _ in cases]
+    torch.cuda.synchronize()
+    results, errors = [None] * len(cases), []
+    start = threading.Barrier(len(cases))
+    rla.set_option(rla.OPT_PATH, 0)
+    rla.set_option(rla.OPT_GATE, 2)  # verify every call
+    before = rla.stats()
+
+    def worker(i):
+        try:
+            shape, split = cases[i]
+            dq, dk = dev_in[i]
+            with rla.tables_build(*shape[1:4], split) as tab:
+                start.wait(timeout=60)
+                outs = []
+                with torch.cuda.stream(streams[i]):
+                    for _ in range(3):
+                        qo, ko = torch.empty_like(dq), torch.empty_like(dk)
+                        rla.apply_qk_noalloc(dq, dk, tab, qo, ko, stream=streams[i])
+                        outs.append((qo, ko))
+                streams[i].synchronize()
+            results[i] = outs
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(e)
+
+    try:
+        threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join(timeout=120)
+    finally:
+        rla.set_option(rla.OPT_GATE, 1)
+    assert not errors, errors
+    after = rla.stats()
+    assert after["gate_verifications"] == before["gate_verifications"] + 3 * len(cases)
+    assert after["gate_disabled"] == before["gate_disabled"]
+    for i, (shape, split) in enumerate(cases):
+        want_q, want_k = oracle.rope3d_qk(*inputs[i], oracle.BF16, split)
+        for qo, ko in results[i]:
+            for got, want in ((qo, want_q), (ko, want_k)):
+                assert np.array_equal(raw(got).cpu().numpy().view(np.uint16), want.view(np.uint16)), (i, shape)
