@@ -352,7 +352,7 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+    emit(line)
     if parity["mismatching_elements"]:
         sys.exit(1)
 
@@ -467,7 +467,7 @@ def main_cycle(args):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": None,
     }
-    print(json.dumps(line), flush=True)
+    emit(line)
     if parity["mismatching_elements"]:
         sys.exit(1)
 
@@ -554,7 +554,7 @@ def main_neox(args):
                      "traffic": measured_traffic(w.key, kernel)},
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+    emit(line)
     if parity["mismatching_elements"]:
         sys.exit(1)
 
@@ -606,7 +606,7 @@ def main_dit(args):
                          "sample": "the float64 recipe, one whole grid per call (exact rationals and 60-digit "
                                    "decimals)"},
     }
-    print(json.dumps(line), flush=True)
+    emit(line)
     if mism:
         sys.exit(1)
 
@@ -701,9 +701,29 @@ def main_patch(args):
                      "frac": round(alg / kavg / 1e9 / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, kernel)},
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+    emit(line)
     if parity["mismatching_elements"]:
         sys.exit(1)
+
+
+def device_info() -> dict:
+    """The GPU the line was measured on, as the HIP runtime reports it (through torch)."""
+    import torch
+
+    p = torch.cuda.get_device_properties(0)
+    out = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+           "hbm_bytes": int(p.total_memory)}
+    for key in ("L2_cache_size", "clock_rate", "memory_clock_rate", "memory_bus_width"):
+        v = getattr(p, key, None)
+        if v is not None:
+            out[key] = int(v)
+    return out
+
+
+def emit(line: dict) -> None:
+    """Prints the one JSON line, with the device it was measured on."""
+    line["device"] = device_info()
+    print(json.dumps(line), flush=True)
 
 
 def device_segments(dev) -> int:
