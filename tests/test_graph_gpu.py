@@ -1,7 +1,8 @@
 """The library's launches inside a HIP graph (torch.cuda.graph capture) and its replays.
 
 Each entry point is called once eagerly (the first call of a configuration runs the gate's
-verification, which synchronizes, and allocates the per-device counter), then captured; the
+verification, which synchronizes, and allocates the per-device counter; the DiT grid needs no
+such call), then captured; the
 graph is replayed several times with fresh inputs copied in by eager work between replays, and
 every replay is compared bit for bit with the oracle.  The captured work is one kernel launch
 per call: nothing in it clears memory with hipMemsetAsync.
@@ -117,6 +118,32 @@ def test_patchify_graph_replays():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(y.cpu().numpy().view(np.uint16), pf.patchify(h, p))
         np.testing.assert_array_equal(back.cpu().numpy().view(np.uint16), h)
+
+
+def test_dit_freq_grid_graph_replays():
+    """Both recipes of the DiT frequency grid captured through the C ABI into fixed outputs; every
+    replay, after the outputs are cleared by eager work, equals the oracle."""
+    import ctypes
+
+    import oracle.dit_freqs as df
+
+    theta, dim, ne = 10000.0, 4096, 6
+    outs = {d: torch.empty(dim // ne, dtype=torch.float32, device=DEV) for d in (1, 0)}
+    n = ctypes.c_int64(0)
+    L = _lib.lib()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sp = torch.cuda.current_stream().cuda_stream
+        for d, out in outs.items():
+            assert L.ltx3drope_dit_freq_grid(theta, dim, ne, d, out.data_ptr(), sp, ctypes.byref(n)) == _lib.OK
+    want = {d: df.freq_grid(theta, dim, ne, bool(d)).view(np.uint32) for d in outs}
+    for _ in range(3):
+        for out in outs.values():
+            out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for d, out in outs.items():
+            np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), want[d])
 
 
 @pytest.mark.parametrize("entry", ["apply_qk", "apply_qk_noalloc"])
