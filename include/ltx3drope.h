@@ -293,7 +293,15 @@ int ltx3drope_apply_qk_shard(void* q_out, void* k_out, const void* q, const void
  * q_out and k_out both NULL (fresh outputs: only the inputs are checked);
  * apply_qk needs both.  tokens = 0 is an empty call: the other sizes and the
  * dtypes are checked, no pointer is looked at (an empty tensor's may be NULL),
- * can_use returns 1 and apply_qk returns OK without launching.  apply_qk returns
+ * can_use returns 1 and apply_qk returns OK without launching.  The rules are
+ * checked in this order and the first that fails names the reason: with
+ * tokens = 0, DTYPE, NONPOSITIVE_DIM (q_heads, k_heads, head_dim or
+ * max_position <= 0), SPLIT_ODD, TOO_LARGE (a size of 2^31 or more, or a cache
+ * of 2^32 elements or more); otherwise NULLPTR, DTYPE, NONPOSITIVE_DIM,
+ * SPLIT_ODD, ALIGN (q_out, k_out, q, k to their element size, the cache to
+ * its own, positions to 8 B), TOO_LARGE, OVERLAP (an output over an input
+ * other than its own exactly, over the other output, the positions or the
+ * cache), then the device-memory rules.  apply_qk returns
  * E_UNSUPPORTED for any of these; the first call on a device allocates the
  * device's 256-byte counter (E_NOMEM when out of memory, E_HIP for another
  * HIP failure), and a failed launch gives E_HIP.
